@@ -1,0 +1,160 @@
+/*
+ * CPU oracle for FP32 row reductions -- TEST INFRASTRUCTURE ONLY.
+ * Definitions and citations are in oracle.h.  Build with
+ *   gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared oracle.c -o liboracle.so -lm
+ * (no fast-math: the FP32 replay needs every operation rounded on its own).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+
+/* Row softmax: the source program of section 1 of "TIRx Metal reduction
+ * lowering" takes exp of the row minus its maximum, then divides by the sum
+ * of those exponentials.  Computed here in double. */
+void oracle_softmax_f64(const float* x, double* y, int64_t rows, int64_t cols) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        double* yr = y + r * cols;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < cols; ++j) {
+            if ((double)xr[j] > m) m = (double)xr[j];
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            double e = exp((double)xr[j] - m);
+            yr[j] = e;
+            s += e;
+        }
+        for (int64_t j = 0; j < cols; ++j) yr[j] = yr[j] / s;
+    }
+}
+
+/* RMSNorm: not written out on the pages (only timed).  Reading used: the
+ * mean of squares over the row, eps added inside the square root (as the
+ * LayerNorm source of section 5.1 adds its eps), gamma applied last. */
+void oracle_rmsnorm_f64(const float* x, const float* gamma, double* y,
+                        int64_t rows, int64_t cols, double eps) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        double* yr = y + r * cols;
+        double ss = 0.0;
+        for (int64_t j = 0; j < cols; ++j) ss += (double)xr[j] * (double)xr[j];
+        double ms = ss / (double)cols;
+        double d = sqrt(ms + eps);
+        for (int64_t j = 0; j < cols; ++j) {
+            double g = gamma ? (double)gamma[j] : 1.0;
+            yr[j] = g * ((double)xr[j] / d);
+        }
+    }
+}
+
+void oracle_layernorm_stats_f64(const float* x, double* mean, double* var,
+                                int64_t rows, int64_t cols) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) s += (double)xr[j];
+        double mu = s / (double)cols;
+        double q = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            double c = (double)xr[j] - mu;
+            q += c * c;
+        }
+        mean[r] = mu;
+        var[r] = q / (double)cols;
+    }
+}
+
+/* LayerNorm: section 5.1 of "TIRx Metal reduction lowering" -- mean = sum/width,
+ * centred = x - mean, variance = sum(centred^2)/width, output centred /
+ * sqrt(variance + eps); the section 8 test applies a per-column affine
+ * (gamma, beta) to those outputs. */
+void oracle_layernorm_f64(const float* x, const float* gamma, const float* beta,
+                          double* y, int64_t rows, int64_t cols, double eps) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        double* yr = y + r * cols;
+        double mu, var;
+        oracle_layernorm_stats_f64(xr, &mu, &var, 1, cols);
+        double d = sqrt(var + eps);
+        for (int64_t j = 0; j < cols; ++j) {
+            double g = gamma ? (double)gamma[j] : 1.0;
+            double b = beta ? (double)beta[j] : 0.0;
+            yr[j] = ((double)xr[j] - mu) / d * g + b;
+        }
+    }
+}
+
+/* Cross-entropy: section 1 composes peak = max(row), total = sum exp(row -
+ * peak), selected = gather(row, label) and stores log(total) + peak -
+ * selected; section 5.2 makes the gather a guarded read of the logits tensor
+ * with fill 0 when the label is outside [0, cols). */
+void oracle_cross_entropy_f64(const float* logits, const int64_t* labels,
+                              double* losses, int64_t rows, int64_t cols) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = logits + r * cols;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < cols; ++j) {
+            if ((double)xr[j] > m) m = (double)xr[j];
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) s += exp((double)xr[j] - m);
+        int64_t l = labels[r];
+        double sel = (l >= 0 && l < cols) ? (double)xr[l] : 0.0;
+        losses[r] = log(s) + m - sel;
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * ordered_fold replay in FP32.  The pages' fold_left restriction (section 1
+ * of "TIRx Metal reduction lowering") keeps a reduction as one ordered chain
+ * and requires precise math; here each chain starts from the add identity
+ * +0.0f and takes elements j = 0, 1, ..., n-1.
+ * ------------------------------------------------------------------------- */
+float oracle_fold_left_f32(const float* x, int64_t n, int kind) {
+    float acc = 0.0f;
+    for (int64_t j = 0; j < n; ++j) {
+        float c = (kind == 1) ? x[j] * x[j] : x[j];
+        acc = acc + c;
+    }
+    return acc;
+}
+
+void oracle_rmsnorm_fold_f32(const float* x, const float* gamma, float* y,
+                             int64_t rows, int64_t cols, float eps) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        float* yr = y + r * cols;
+        float acc = oracle_fold_left_f32(xr, cols, 1);
+        float ms = acc / (float)cols;
+        float rr = 1.0f / sqrtf(ms + eps);
+        for (int64_t j = 0; j < cols; ++j) {
+            float t = xr[j] * rr;
+            yr[j] = gamma ? t * gamma[j] : t;
+        }
+    }
+}
+
+void oracle_layernorm_fold_f32(const float* x, const float* gamma,
+                               const float* beta, float* y, int64_t rows,
+                               int64_t cols, float eps) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        float* yr = y + r * cols;
+        float mu = oracle_fold_left_f32(xr, cols, 0) / (float)cols;
+        float acc = 0.0f;
+        for (int64_t j = 0; j < cols; ++j) {
+            float c = xr[j] - mu;
+            acc = acc + c * c;
+        }
+        float var = acc / (float)cols;
+        float rr = 1.0f / sqrtf(var + eps);
+        for (int64_t j = 0; j < cols; ++j) {
+            float t = (xr[j] - mu) * rr;
+            if (gamma) t = t * gamma[j];
+            if (beta) t = t + beta[j];
+            yr[j] = t;
+        }
+    }
+}
