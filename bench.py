@@ -1,0 +1,349 @@
+"""Benchmark of the FP32 row-reduction hot path on one MI355X.
+
+One step = softmax, RMSNorm and LayerNorm, each on a 768 x 6144 FP32 tensor
+(x ~ N(0,1), gamma ~ U(0.5,1.5), beta ~ N(0, 0.1^2), eps 1e-6 / 1e-5), launched
+through the C ABI on the current torch stream.  Inputs are device-resident
+before timing.  By default every launch reads a different buffer set out of
+32 rotating sets (1.2 GB in total, larger than the 256 MB Infinity Cache and
+the L2s), so each launch streams its tensor from HBM ("cold").
+
+Printed: one JSON line with throughput (GB/s of algorithmic bytes = tensor
+read + tensor write per op), per-op microseconds, the roofline record of the
+dominant kernel (its average launch duration: HIP events around a batch of
+back-to-back cold launches of that kernel alone), the oracle's CPU baseline
+and, as context,
+warm-cache and cross-entropy 4096 x 32000 figures.
+
+    python bench.py [--steps K] [--warmup W] [--warm] [--no-cpu-baseline]
+                    [--no-extra] [--copy-probe]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+ROWS, COLS = 768, 6144
+OPS = ("softmax", "rmsnorm", "layernorm")
+EPS = {"rmsnorm": 1e-6, "layernorm": 1e-5}
+HBM_PEAK_GBS = 8000.0
+METRIC = "µs/op + achieved HBM GB/s (% of peak), FP32 softmax/RMSNorm/LayerNorm 768×6144"
+# The pages' M1 Max command-buffer medians at 768x6144 (softmax, RMSNorm,
+# LayerNorm): 57.414 + 60.753 + 75.251 us for the three ops' algorithmic bytes.
+PAGES_M1MAX_STEP_US = 57.414 + 60.753 + 75.251
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_768x6144.json")
+
+
+def traffic_bytes(op: str):
+    """HBM bytes per launch of `op` from the committed FETCH_SIZE / WRITE_SIZE
+    summary (copy-calibrated), or None when the kernels changed since."""
+    from row_reductions_amd import profiling
+    rec = profiling.lookup(TRAFFIC_SUMMARY, op)
+    return None if rec is None else round(rec["traffic_bytes"])
+
+
+def op_bytes(rows: int, cols: int) -> int:
+    """Algorithmic bytes of one softmax / norm launch: read + write of the tensor."""
+    return 2 * rows * cols * 4
+
+
+def ce_bytes(rows: int, cols: int) -> int:
+    """Cross-entropy: logits read, int64 labels read, FP32 losses written."""
+    return rows * cols * 4 + rows * 8 + rows * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--sets", type=int, default=32, help="rotating buffer sets per op (cold cache)")
+    ap.add_argument("--warm", action="store_true", help="time one buffer set (cache-warm) as the main figure")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work budget of the oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the warm and cross-entropy context figures")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also launch a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the row-reduction path has no multi-GPU part "
+              "(rows are independent; sharding is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import row_reductions_amd as lr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    # ---------------- inputs (seeded, device-resident) ----------------
+    soft = synth.softmax_inputs(ROWS, COLS, seed=0)
+    rms = synth.rmsnorm_inputs(ROWS, COLS, seed=0)
+    ln = synth.layernorm_inputs(ROWS, COLS, seed=0)
+    nsets = 1 if args.warm else args.sets
+
+    def device_sets(x: np.ndarray):
+        xt = torch.from_numpy(x).to(dev)
+        xs = [xt] + [xt.clone() for _ in range(nsets - 1)]
+        ys = [torch.empty_like(xt) for _ in range(nsets)]
+        return xs, ys
+
+    sx, sy = device_sets(soft["x"])
+    rx, ry = device_sets(rms["x"])
+    lx, ly = device_sets(ln["x"])
+    rg = torch.from_numpy(rms["gamma"]).to(dev)
+    lg = torch.from_numpy(ln["gamma"]).to(dev)
+    lb = torch.from_numpy(ln["beta"]).to(dev)
+
+    def launch(op: str, i: int) -> None:
+        k = i % nsets
+        if op == "softmax":
+            st = lr.lib.lr_softmax_f32(sx[k].data_ptr(), sy[k].data_ptr(), ROWS, COLS, 0, sh)
+        elif op == "rmsnorm":
+            st = lr.lib.lr_rmsnorm_f32(rx[k].data_ptr(), rg.data_ptr(), ry[k].data_ptr(), ROWS, COLS,
+                                       EPS["rmsnorm"], 0, sh)
+        else:
+            st = lr.lib.lr_layernorm_f32(lx[k].data_ptr(), lg.data_ptr(), lb.data_ptr(), ly[k].data_ptr(),
+                                         ROWS, COLS, EPS["layernorm"], 0, sh)
+        if st != 0:
+            raise lr.LrError(st, op)
+
+    # ---------------- warmup ----------------
+    for i in range(args.warmup):
+        for op in OPS:
+            launch(op, i)
+    torch.cuda.synchronize()
+
+    # ---------------- timed region: K steps ----------------
+    # events only at the edges: a marker between kernels would serialise the
+    # stream and add its own gap to every launch
+    K = args.steps
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        for op in OPS:
+            launch(op, i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    gpu_ms_per_step = t_start.elapsed_time(t_end) / K
+
+    # per-kernel average launch duration: each op alone, K back-to-back cold
+    # launches on the same stream, HIP events around the batch
+    per_op_us = {}
+    for op in OPS:
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(10):
+            launch(op, i)
+        a.record(stream)
+        for i in range(K):
+            launch(op, i)
+        z.record(stream)
+        torch.cuda.synchronize()
+        per_op_us[op] = a.elapsed_time(z) * 1e3 / K
+
+    b = op_bytes(ROWS, COLS)
+    step_bytes = b * len(OPS)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    gbps = {op: b / (per_op_us[op] * 1e-6) / 1e9 for op in OPS}
+    dominant = max(OPS, key=lambda o: per_op_us[o])
+    achieved = gbps[dominant]
+
+    # single-call latency: one launch between synchronisations
+    single = {}
+    for op in OPS:
+        vals = []
+        for i in range(20):
+            torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch(op, i)
+            z.record(stream)
+            torch.cuda.synchronize()
+            vals.append(a.elapsed_time(z) * 1e3)
+        single[op] = float(np.median(vals))
+
+    plans = {}
+    for op in OPS:
+        p = lr.lr_plan_query(op, ROWS, COLS, "unordered_tree")
+        plans[op] = {k: v for k, v in p.as_dict().items() if k in (
+            "family", "waves_per_row", "rows_per_block", "chunks_per_lane", "threads_per_block", "blocks")}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (step_bytes / (PAGES_M1MAX_STEP_US * 1e-6) / 1e9), 3),
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "softmax + RMSNorm + LayerNorm, FP32 768x6144 each (x~N(0,1), gamma~U(0.5,1.5), "
+                        "beta~N(0,0.1^2), eps 1e-6/1e-5), unordered_tree",
+            "rows": ROWS, "cols": COLS, "ops": list(OPS), "policy": "unordered_tree",
+            "cache_state": ("warm (one buffer set)" if args.warm else
+                            f"cold ({nsets} rotating buffer sets per op, "
+                            f"{nsets * b * len(OPS) / 1e9:.2f} GB)"),
+            "bytes_per_step": step_bytes,
+            "vs_baseline_note": "ratio to the pages' Apple M1 Max command-buffer medians "
+                                "(57.414/60.753/75.251 us); context, not a target",
+        },
+        "us_per_op": {op: round(per_op_us[op], 3) for op in OPS},
+        "single_call_us": single,
+        "gbps_per_op": {op: round(gbps[op], 1) for op in OPS},
+        "pct_of_hbm_peak_per_op": {op: round(100 * gbps[op] / HBM_PEAK_GBS, 2) for op in OPS},
+        "plans": plans,
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_bytes(dominant),
+            "bytes_per_launch": b,
+            "avg_launch_us": round(per_op_us[dominant], 3),
+        },
+    }
+
+    # ---------------- context: warm cache and cross-entropy ----------------
+    if not args.no_extra:
+        extra = {}
+        if not args.warm:
+            n = 400
+            for op in OPS:
+                for i in range(20):
+                    launch(op, 0)
+                torch.cuda.synchronize()
+                a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for i in range(n):
+                    launch(op, 0)
+                z.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(z) * 1e3 / n
+                extra[f"{op}_768x6144_warm"] = {"us_per_op": round(us, 3), "gbps": round(b / us / 1e3, 1)}
+        ce = synth.cross_entropy_inputs(4096, 32000, seed=0)
+        cx = [torch.from_numpy(ce["logits"]).to(dev)]
+        cx.append(cx[0].clone())
+        clab = torch.from_numpy(ce["labels"]).to(dev)
+        closs = torch.empty(4096, device=dev)
+        del ce
+        n = 100
+        for i in range(10):
+            lr.check(lr.lib.lr_cross_entropy_f32(cx[i % 2].data_ptr(), clab.data_ptr(), closs.data_ptr(),
+                                                 4096, 32000, 0, sh))
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            lr.lib.lr_cross_entropy_f32(cx[i % 2].data_ptr(), clab.data_ptr(), closs.data_ptr(), 4096, 32000,
+                                        0, sh)
+        z.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(z) * 1e3 / n
+        cb = ce_bytes(4096, 32000)
+        p = lr.lr_plan_query("cross_entropy", 4096, 32000)
+        extra["cross_entropy_4096x32000_cold"] = {
+            "us_per_op": round(us, 3), "gbps": round(cb / us / 1e3, 1),
+            "pct_of_hbm_peak": round(100 * cb / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": cb,
+            "plan": {k: v for k, v in p.as_dict().items() if k in (
+                "family", "waves_per_row", "rows_per_block", "chunks_per_lane", "threads_per_block")}}
+        del cx
+        out["extra"] = extra
+
+    if args.copy_probe:
+        # plain device-to-device copies of one 768x6144 tensor: the reference
+        # kernel for scaling FETCH_SIZE / WRITE_SIZE counters to bytes
+        for _ in range(20):
+            sy[0].copy_(sx[0])
+        torch.cuda.synchronize()
+
+    # ---------------- CPU baseline: the oracle on the host cores ----------------
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(soft, rms, ln, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+def cpu_baseline(soft, rms, ln, budget_s: float) -> dict:
+    """The double-precision oracle, unmodified, on the same 768x6144 inputs.
+    Rows are split over host threads (the C oracle releases the GIL); the
+    whole three-op workload is repeated until `budget_s` seconds are used."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+
+    cores = min(16, os.cpu_count() or 1)
+    chunks = np.array_split(np.arange(ROWS), cores)
+
+    def run_rows(idx):
+        lo, hi = int(idx[0]), int(idx[-1]) + 1
+        oracle.softmax(soft["x"][lo:hi])
+        oracle.rmsnorm(rms["x"][lo:hi], rms["gamma"], EPS["rmsnorm"])
+        oracle.layernorm(ln["x"][lo:hi], ln["gamma"], ln["beta"], EPS["layernorm"])
+
+    reps = 0
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(run_rows, chunks))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                break
+    step_s = el / reps
+    step_bytes = op_bytes(ROWS, COLS) * len(OPS)
+    return {
+        "value": round(step_bytes / step_s / 1e9, 3),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"full workload (softmax+RMSNorm+LayerNorm 768x6144), {reps} repetitions in {el:.1f} s, "
+                  f"rows split over {cores} threads; {step_s * 1e3:.2f} ms per step",
+        "cpu": _cpu_model(),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,242 @@
+/*
+ * lr.h -- C ABI of the MI355X (gfx950) FP32 row-reduction library, liblr.so.
+ *
+ * Four row operations over a row-major rows x cols FP32 tensor (row stride =
+ * cols elements).  Each is a composition of max/add folds over the column
+ * axis, as defined on the page "TIRx Metal reduction lowering"
+ * (LuisaCompute), section 1 (softmax and cross-entropy sources), section 5.1
+ * (LayerNorm statistics), section 5.2 (guarded label gather).  The
+ * reduction-order contract (unordered tree versus ordered fold) is the
+ * ReductionPolicy of section 1.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   All tensor pointers are DEVICE pointers owned by the caller.  The
+ *           library allocates no device memory, keeps no device state and
+ *           never reads or writes outside the ranges described per call.
+ *           FP32 pointers must be 4-byte aligned and the int64 label pointer
+ *           8-byte aligned (else LR_ERR_MISALIGNED); 16-byte alignment is not
+ *           required (misaligned rows take a guarded path).
+ * Aliasing. Inputs and outputs must not overlap, except that an operation's
+ *           output may be exactly its input tensor (y == x: in place).  Any
+ *           other overlap returns LR_ERR_ALIASING (the pages' kernel ABI is
+ *           noalias, section 3).
+ * Shapes.   rows >= 0, cols >= 1, rows*cols*4 must fit in int64, cols < 2^24
+ *           (so that cols is exact in FP32).  rows == 0 returns LR_OK and
+ *           launches nothing.
+ * Streams.  Work is enqueued on `stream` (NULL = the default stream) and the
+ *           call returns without synchronising.  A launch failure reported
+ *           by the HIP runtime returns LR_ERR_HIP.
+ * Errors.   Every argument is validated before any HIP call; nothing falls
+ *           back to the CPU.  An explicit plan that cannot be realised
+ *           returns LR_ERR_UNREALIZABLE_PLAN; it is never clamped.
+ * Threads.  All entry points are thread-safe.
+ * Policy.   LR_UNORDERED_TREE lets every add/max fold be reassociated (lane
+ *           stripes, then a wave64 tree, then a cross-wave tree) and lets the
+ *           kernels use hardware exp/rcp/rsqrt; results are still bitwise
+ *           repeatable for a fixed plan.  LR_ORDERED_FOLD makes every add
+ *           fold one FP32 left-to-right chain per row (j = 0 .. cols-1, each
+ *           operation rounded on its own, no fused multiply-add), uses IEEE
+ *           division and square root, and fixes the elementwise order; its
+ *           result does not depend on the plan.  Max folds are exact in any
+ *           order under both policies.
+ */
+#ifndef LR_H
+#define LR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum lr_reduction_policy {
+    LR_UNORDERED_TREE = 0,
+    LR_ORDERED_FOLD = 1
+} lr_reduction_policy;
+
+typedef enum lr_status {
+    LR_OK = 0,
+    LR_ERR_NULL_POINTER = 1,
+    LR_ERR_INVALID_SHAPE = 2,
+    LR_ERR_INVALID_EPS = 3,
+    LR_ERR_INVALID_POLICY = 4,
+    LR_ERR_MISALIGNED = 5,
+    LR_ERR_ALIASING = 6,
+    LR_ERR_UNREALIZABLE_PLAN = 7,
+    LR_ERR_HIP = 8,
+    LR_ERR_INVALID_ARGUMENT = 9
+} lr_status;
+
+typedef enum lr_op {
+    LR_OP_SOFTMAX = 0,
+    LR_OP_RMSNORM = 1,
+    LR_OP_LAYERNORM = 2,
+    LR_OP_CROSS_ENTROPY = 3
+} lr_op;
+
+/* Kernel families.
+ * CACHE:   each lane keeps its stripe of the row in registers (VGPRs), so
+ *          the row is read from memory once and every later pass reads
+ *          registers (the pages' worker-private stripe, section 5).
+ * STREAM:  no register copy; passes that need the row again reload it
+ *          (softmax and cross-entropy fold max and sum-of-exp in one
+ *          online pass).  Any row length.
+ * ORDERED: the LR_ORDERED_FOLD realisation: one wavefront per row, the row
+ *          staged through LDS in 256-element slabs and folded in order. */
+typedef enum lr_family {
+    LR_FAMILY_CACHE = 0,
+    LR_FAMILY_STREAM = 1,
+    LR_FAMILY_ORDERED = 2
+} lr_family;
+
+/* A launch plan (the pages' GroupPlan decision record, section 2, mapped to
+ * wave64: workers per row W = 64 * waves_per_row, section 4). */
+typedef struct lr_plan {
+    int32_t family;            /* lr_family */
+    int32_t waves_per_row;     /* S: wavefronts cooperating on one row, 1..16 */
+    int32_t rows_per_block;    /* Q: rows packed into one workgroup, S*Q <= 16 */
+    int32_t vec;               /* V: consecutive FP32 a lane owns per chunk (4 = 128-bit) */
+    int32_t chunks_per_lane;   /* CACHE: 128-bit chunks held per lane (a compiled
+                                  instance: 1,2,3,4,6,8,12,16,24 or 32);
+                                  STREAM: chunks loaded per lane per loop trip;
+                                  ORDERED: 0 */
+    int32_t threads_per_block; /* 64 * S * Q */
+    int64_t blocks;            /* ceil(rows / Q) */
+    int32_t lds_bytes;         /* static LDS the kernel uses */
+    int32_t reductions;        /* |R|: cross-lane reductions per row */
+    int32_t row_aligned;       /* 1: planned for 16-byte aligned rows */
+    int32_t reserved;
+} lr_plan;
+
+/* What the planner needs to know about a device. */
+typedef struct lr_device_facts {
+    int32_t compute_units;          /* 256 on MI355X */
+    int32_t max_threads_per_block;  /* 1024 */
+    int32_t simds_per_cu;           /* 4 */
+    int32_t wave_size;              /* 64 */
+} lr_device_facts;
+
+/* ---------------------------------------------------------------------------
+ * Operations
+ * ------------------------------------------------------------------------- */
+
+/* Row softmax ("TIRx Metal reduction lowering", section 1, softmax source):
+ *   y[r][j] = exp(x[r][j] - m_r) / sum_k exp(x[r][k] - m_r),  m_r = max_k x[r][k].
+ * x: rows*cols FP32 in; y: rows*cols FP32 out (y == x allowed). */
+lr_status lr_softmax_f32(const float* x, float* y, int64_t rows, int64_t cols,
+                         lr_reduction_policy policy, hipStream_t stream);
+
+/* RMSNorm (timed on the page "Whole-launch reduction cost policy", held-out
+ * table; no formula on the pages -- eps inside the root as LayerNorm does in
+ * section 5.1):
+ *   y[r][j] = gamma[j] * x[r][j] / sqrt(mean_k x[r][k]^2 + eps).
+ * gamma: cols FP32, or NULL for 1.  eps: finite, >= 0 (else LR_ERR_INVALID_EPS).
+ * Under LR_ORDERED_FOLD the FP32 sequence is ss = fold(x*x), ms = ss/cols,
+ * r = 1/sqrt(ms + eps), y = (x*r)*gamma. */
+lr_status lr_rmsnorm_f32(const float* x, const float* gamma, float* y,
+                         int64_t rows, int64_t cols, float eps,
+                         lr_reduction_policy policy, hipStream_t stream);
+
+/* LayerNorm ("TIRx Metal reduction lowering", section 5.1 statistics, section
+ * 8 affine):  mu = sum_k x/cols;  var = sum_k (x - mu)^2 / cols (biased,
+ * centred two-pass);  y = (x - mu) / sqrt(var + eps) * gamma + beta.
+ * gamma, beta: cols FP32 each, or NULL for 1 / 0.  eps: finite, >= 0.
+ * Under LR_ORDERED_FOLD: mu = fold(x)/cols, var = fold((x-mu)*(x-mu))/cols,
+ * r = 1/sqrt(var + eps), y = ((x-mu)*r)*gamma + beta (absent terms skipped). */
+lr_status lr_layernorm_f32(const float* x, const float* gamma, const float* beta,
+                           float* y, int64_t rows, int64_t cols, float eps,
+                           lr_reduction_policy policy, hipStream_t stream);
+
+/* Per-row cross-entropy ("TIRx Metal reduction lowering", section 1
+ * cross-entropy source; section 5.2 guarded gather):
+ *   m = max_k x[r][k];  s = sum_k exp(x[r][k] - m);
+ *   sel = (0 <= labels[r] < cols) ? x[r][labels[r]] : 0   (int64 compare);
+ *   losses[r] = log(s) + m - sel.
+ * logits: rows*cols FP32; labels: rows int64 (any value: out-of-range labels
+ * are not an error, they select 0); losses: rows FP32 out. */
+lr_status lr_cross_entropy_f32(const float* logits, const int64_t* labels,
+                               float* losses, int64_t rows, int64_t cols,
+                               lr_reduction_policy policy, hipStream_t stream);
+
+/* The same four operations under an explicit plan (the pages' exact
+ * thread/packing constraints, section 6: honoured exactly or rejected).
+ * `plan->family` must be LR_FAMILY_ORDERED exactly when policy is
+ * LR_ORDERED_FOLD.  A plan that does not cover the row, exceeds a device
+ * limit or names a chunk count with no compiled instance returns
+ * LR_ERR_UNREALIZABLE_PLAN before any launch. */
+lr_status lr_softmax_f32_with_plan(const float* x, float* y, int64_t rows, int64_t cols,
+                                   lr_reduction_policy policy, const lr_plan* plan,
+                                   hipStream_t stream);
+lr_status lr_rmsnorm_f32_with_plan(const float* x, const float* gamma, float* y,
+                                   int64_t rows, int64_t cols, float eps,
+                                   lr_reduction_policy policy, const lr_plan* plan,
+                                   hipStream_t stream);
+lr_status lr_layernorm_f32_with_plan(const float* x, const float* gamma, const float* beta,
+                                     float* y, int64_t rows, int64_t cols, float eps,
+                                     lr_reduction_policy policy, const lr_plan* plan,
+                                     hipStream_t stream);
+lr_status lr_cross_entropy_f32_with_plan(const float* logits, const int64_t* labels,
+                                         float* losses, int64_t rows, int64_t cols,
+                                         lr_reduction_policy policy, const lr_plan* plan,
+                                         hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Planner (host only; no device memory touched)
+ * ------------------------------------------------------------------------- */
+
+/* Facts of the current HIP device (hipGetDeviceProperties).  LR_ERR_HIP when
+ * no device is usable. */
+lr_status lr_device_facts_query(lr_device_facts* out);
+
+/* Facts of an MI355X, for planning without a device. */
+void lr_device_facts_mi355x(lr_device_facts* out);
+
+/* The plan an operation launches with on the current device, assuming
+ * 16-byte aligned tensor bases. */
+lr_status lr_plan_query(lr_op op, int64_t rows, int64_t cols,
+                        lr_reduction_policy policy, lr_plan* out);
+
+/* Pure planner: the automatic plan for `facts`.  row_aligned = 1 when every
+ * row starts 16-byte aligned (cols % 4 == 0 and aligned bases). */
+lr_status lr_plan_for_device(const lr_device_facts* facts, lr_op op, int64_t rows,
+                             int64_t cols, lr_reduction_policy policy,
+                             int32_t row_aligned, lr_plan* out);
+
+/* Every legal plan, in enumeration order (family, S, Q).  Writes at most
+ * `capacity` plans to `out` (out may be NULL when capacity is 0) and the
+ * total number of legal plans to *count. */
+lr_status lr_plan_enumerate(const lr_device_facts* facts, lr_op op, int64_t rows,
+                            int64_t cols, lr_reduction_policy policy,
+                            int32_t row_aligned, lr_plan* out, int32_t capacity,
+                            int32_t* count);
+
+/* LR_OK when `plan` is realisable for this problem on `facts`, else the
+ * reason (LR_ERR_UNREALIZABLE_PLAN or an argument error). */
+lr_status lr_plan_validate(const lr_device_facts* facts, lr_op op, int64_t rows,
+                           int64_t cols, lr_reduction_policy policy,
+                           int32_t row_aligned, const lr_plan* plan);
+
+/* Host replay of a plan's thread -> element mapping (the same index functions
+ * the kernels are compiled from): adds 1 to counts[r*cols + e] for every
+ * (row r, element e) some thread of the launch owns, for rows whose first
+ * element sits `phase` floats past a 16-byte boundary when r == 0 (each later
+ * row shifted by cols).  counts: rows*cols uint32 host array.  Used to prove
+ * that each element is covered exactly once (section 4.4 of the pages). */
+lr_status lr_coverage_check(const lr_plan* plan, int64_t rows, int64_t cols,
+                            int32_t phase, uint32_t* counts);
+
+/* Human-readable name of a status code (static storage). */
+const char* lr_status_string(lr_status status);
+
+/* Library version string, e.g. "lr 0.1.0 gfx950". */
+const char* lr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LR_H */

@@ -1,0 +1,252 @@
+// C-ABI entry points of liblr.so: argument validation (before any HIP
+// call), plan selection, kernel dispatch and status mapping.  Declarations
+// and the full contract are in include/lr.h.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "lr_internal.hpp"
+#include "lr_map.hpp"
+
+namespace lr {
+
+lr_status validate_plan(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy,
+                        bool aligned, const lr_plan* p);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_facts_mu;
+bool g_facts_ok[kMaxDevices];
+lr_device_facts g_facts[kMaxDevices];
+
+lr_status current_facts(lr_device_facts* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LR_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_facts_mu);
+    if (!g_facts_ok[dev]) {
+        int cus = 0, maxt = 0, ws = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&maxt, hipDeviceAttributeMaxThreadsPerBlock, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&ws, hipDeviceAttributeWarpSize, dev) != hipSuccess)
+            return LR_ERR_HIP;
+        lr_device_facts f;
+        f.compute_units = cus;
+        f.max_threads_per_block = maxt;
+        f.simds_per_cu = 4;
+        f.wave_size = ws;
+        g_facts[dev] = f;
+        g_facts_ok[dev] = true;
+    }
+    *out = g_facts[dev];
+    return LR_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Call {
+    int op;
+    const float* x;
+    const float* gamma;
+    const float* beta;
+    float* y;
+    const int64_t* labels;
+    float* losses;
+    int64_t rows;
+    int64_t cols;
+    float eps;
+    int policy;
+};
+
+lr_status validate_call(const Call& c) {
+    if (c.policy != LR_UNORDERED_TREE && c.policy != LR_ORDERED_FOLD) return LR_ERR_INVALID_POLICY;
+    const bool ce = c.op == LR_OP_CROSS_ENTROPY;
+    if (c.x == nullptr) return LR_ERR_NULL_POINTER;
+    if (ce ? (c.labels == nullptr || c.losses == nullptr) : c.y == nullptr) return LR_ERR_NULL_POINTER;
+    if (c.rows < 0 || c.cols < 1 || c.cols >= (int64_t(1) << 24) || c.rows > INT32_MAX) return LR_ERR_INVALID_SHAPE;
+    if (c.rows > INT64_MAX / 4 / c.cols) return LR_ERR_INVALID_SHAPE;
+    if (c.op == LR_OP_RMSNORM || c.op == LR_OP_LAYERNORM) {
+        if (!std::isfinite(c.eps) || c.eps < 0.0f) return LR_ERR_INVALID_EPS;
+    }
+    auto a4 = [](const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (!a4(c.x) || !a4(c.y) || !a4(c.gamma) || !a4(c.beta) || !a4(c.losses)) return LR_ERR_MISALIGNED;
+    if (c.labels != nullptr && (reinterpret_cast<uintptr_t>(c.labels) & 7u) != 0) return LR_ERR_MISALIGNED;
+    const int64_t tb = c.rows * c.cols * 4;
+    const Range rx = range_of(c.x, tb);
+    if (ce) {
+        const Range rl = range_of(c.losses, c.rows * 4), rlab = range_of(c.labels, c.rows * 8);
+        if (c.rows > 0 && (overlap(rl, rx) || overlap(rl, rlab))) return LR_ERR_ALIASING;
+    } else if (c.rows > 0) {
+        const Range ry = range_of(c.y, tb);
+        if (c.y != c.x && overlap(ry, rx)) return LR_ERR_ALIASING;
+        if (c.gamma != nullptr && overlap(ry, range_of(c.gamma, c.cols * 4))) return LR_ERR_ALIASING;
+        if (c.beta != nullptr && overlap(ry, range_of(c.beta, c.cols * 4))) return LR_ERR_ALIASING;
+    }
+    return LR_OK;
+}
+
+lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
+    lr_status st = validate_call(c);
+    if (st != LR_OK) return st;
+    if (c.rows == 0) return LR_OK;  // nothing to launch
+    const bool ce = c.op == LR_OP_CROSS_ENTROPY;
+    const bool rows_aligned = c.cols % kVec == 0 && aligned16(c.x);
+    const bool aligned = rows_aligned && (ce || (aligned16(c.y) && aligned16(c.gamma) && aligned16(c.beta)));
+
+    lr_device_facts facts;
+    st = current_facts(&facts);
+    if (st != LR_OK) return st;
+    lr_plan plan;
+    if (forced != nullptr) {
+        st = validate_plan(&facts, c.op, c.rows, c.cols, c.policy, rows_aligned, forced);
+        if (st != LR_OK) return st;
+        plan = *forced;
+    } else {
+        st = lr_plan_for_device(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
+                                rows_aligned ? 1 : 0, &plan);
+        if (st != LR_OK) return st;
+    }
+
+    KArgs a;
+    a.x = c.x;
+    a.y = c.y;
+    a.gamma = c.gamma;
+    a.beta = c.beta;
+    a.labels = c.labels;
+    a.losses = c.losses;
+    a.rows = c.rows;
+    a.cols = (int32_t)c.cols;
+    a.eps = c.eps;
+    a.inv_cols = 1.0f / (float)c.cols;
+    a.S = plan.waves_per_row;
+    a.Q = plan.rows_per_block;
+    a.y_same_phase = ce ? 1
+                        : (int32_t)((reinterpret_cast<uintptr_t>(c.y) & 15u) ==
+                                    (reinterpret_cast<uintptr_t>(c.x) & 15u));
+
+    (void)hipGetLastError();  // clear a stale error so the launch's own status is seen
+    hipError_t e;
+    if (plan.family == LR_FAMILY_ORDERED) {
+        e = launch_ordered(c.op, a, plan, stream);
+    } else {
+        switch (c.op) {
+            case LR_OP_SOFTMAX: e = launch_softmax(a, plan, aligned, stream); break;
+            case LR_OP_RMSNORM: e = launch_rmsnorm(a, plan, aligned, stream); break;
+            case LR_OP_LAYERNORM: e = launch_layernorm(a, plan, aligned, stream); break;
+            default: e = launch_cross_entropy(a, plan, aligned, stream); break;
+        }
+    }
+    return e == hipSuccess ? LR_OK : LR_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace lr
+
+using lr::Call;
+
+extern "C" {
+
+lr_status lr_softmax_f32(const float* x, float* y, int64_t rows, int64_t cols, lr_reduction_policy policy,
+                         hipStream_t stream) {
+    return lr::run(Call{LR_OP_SOFTMAX, x, nullptr, nullptr, y, nullptr, nullptr, rows, cols, 0.0f, policy},
+                   nullptr, stream);
+}
+
+lr_status lr_rmsnorm_f32(const float* x, const float* gamma, float* y, int64_t rows, int64_t cols, float eps,
+                         lr_reduction_policy policy, hipStream_t stream) {
+    return lr::run(Call{LR_OP_RMSNORM, x, gamma, nullptr, y, nullptr, nullptr, rows, cols, eps, policy},
+                   nullptr, stream);
+}
+
+lr_status lr_layernorm_f32(const float* x, const float* gamma, const float* beta, float* y, int64_t rows,
+                           int64_t cols, float eps, lr_reduction_policy policy, hipStream_t stream) {
+    return lr::run(Call{LR_OP_LAYERNORM, x, gamma, beta, y, nullptr, nullptr, rows, cols, eps, policy},
+                   nullptr, stream);
+}
+
+lr_status lr_cross_entropy_f32(const float* logits, const int64_t* labels, float* losses, int64_t rows,
+                               int64_t cols, lr_reduction_policy policy, hipStream_t stream) {
+    return lr::run(
+        Call{LR_OP_CROSS_ENTROPY, logits, nullptr, nullptr, nullptr, labels, losses, rows, cols, 0.0f, policy},
+        nullptr, stream);
+}
+
+static lr_status need_plan(const lr_plan* plan) { return plan == nullptr ? LR_ERR_NULL_POINTER : LR_OK; }
+
+lr_status lr_softmax_f32_with_plan(const float* x, float* y, int64_t rows, int64_t cols,
+                                   lr_reduction_policy policy, const lr_plan* plan, hipStream_t stream) {
+    if (need_plan(plan) != LR_OK) return LR_ERR_NULL_POINTER;
+    return lr::run(Call{LR_OP_SOFTMAX, x, nullptr, nullptr, y, nullptr, nullptr, rows, cols, 0.0f, policy},
+                   plan, stream);
+}
+
+lr_status lr_rmsnorm_f32_with_plan(const float* x, const float* gamma, float* y, int64_t rows, int64_t cols,
+                                   float eps, lr_reduction_policy policy, const lr_plan* plan,
+                                   hipStream_t stream) {
+    if (need_plan(plan) != LR_OK) return LR_ERR_NULL_POINTER;
+    return lr::run(Call{LR_OP_RMSNORM, x, gamma, nullptr, y, nullptr, nullptr, rows, cols, eps, policy}, plan,
+                   stream);
+}
+
+lr_status lr_layernorm_f32_with_plan(const float* x, const float* gamma, const float* beta, float* y,
+                                     int64_t rows, int64_t cols, float eps, lr_reduction_policy policy,
+                                     const lr_plan* plan, hipStream_t stream) {
+    if (need_plan(plan) != LR_OK) return LR_ERR_NULL_POINTER;
+    return lr::run(Call{LR_OP_LAYERNORM, x, gamma, beta, y, nullptr, nullptr, rows, cols, eps, policy}, plan,
+                   stream);
+}
+
+lr_status lr_cross_entropy_f32_with_plan(const float* logits, const int64_t* labels, float* losses,
+                                         int64_t rows, int64_t cols, lr_reduction_policy policy,
+                                         const lr_plan* plan, hipStream_t stream) {
+    if (need_plan(plan) != LR_OK) return LR_ERR_NULL_POINTER;
+    return lr::run(
+        Call{LR_OP_CROSS_ENTROPY, logits, nullptr, nullptr, nullptr, labels, losses, rows, cols, 0.0f, policy},
+        plan, stream);
+}
+
+lr_status lr_device_facts_query(lr_device_facts* out) {
+    if (out == nullptr) return LR_ERR_NULL_POINTER;
+    return lr::current_facts(out);
+}
+
+lr_status lr_plan_query(lr_op op, int64_t rows, int64_t cols, lr_reduction_policy policy, lr_plan* out) {
+    if (out == nullptr) return LR_ERR_NULL_POINTER;
+    lr_device_facts f;
+    lr_status st = lr::current_facts(&f);
+    if (st != LR_OK) return st;
+    return lr_plan_for_device(&f, op, rows, cols, policy, 1, out);
+}
+
+const char* lr_status_string(lr_status s) {
+    switch (s) {
+        case LR_OK: return "LR_OK";
+        case LR_ERR_NULL_POINTER: return "LR_ERR_NULL_POINTER: a required pointer is null";
+        case LR_ERR_INVALID_SHAPE: return "LR_ERR_INVALID_SHAPE: rows/cols out of range";
+        case LR_ERR_INVALID_EPS: return "LR_ERR_INVALID_EPS: eps must be finite and >= 0";
+        case LR_ERR_INVALID_POLICY: return "LR_ERR_INVALID_POLICY: unknown reduction policy";
+        case LR_ERR_MISALIGNED: return "LR_ERR_MISALIGNED: pointer not aligned to its element";
+        case LR_ERR_ALIASING: return "LR_ERR_ALIASING: input and output ranges overlap";
+        case LR_ERR_UNREALIZABLE_PLAN: return "LR_ERR_UNREALIZABLE_PLAN: plan cannot be realised as given";
+        case LR_ERR_HIP: return "LR_ERR_HIP: the HIP runtime reported an error";
+        case LR_ERR_INVALID_ARGUMENT: return "LR_ERR_INVALID_ARGUMENT: invalid argument";
+        default: return "unknown lr_status";
+    }
+}
+
+const char* lr_version(void) { return "lr 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// Device helpers for gfx950: wave64 cross-lane reductions, the cross-wave
+// combine through LDS and 128-bit global accesses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "lr_map.hpp"
+
+namespace lr {
+
+enum Op : int { kSoftmax = 0, kRmsNorm = 1, kLayerNorm = 2, kCrossEntropy = 3 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Wave64 all-reduce.  Within each 16-lane DPP row: xor-1 and xor-2 quad
+// permutes, then the half-row mirror and the row mirror, after which all 16
+// lanes of a row hold the row's total.  Rows are then paired with gfx950's
+// v_permlane16_swap (rows 0<->1, 2<->3) and halves with v_permlane32_swap:
+// adding the two swapped copies gives every lane the pair total.  Each step
+// combines the same two partials in every lane (only operand order differs,
+// and add/max commute), so all 64 lanes finish with the same bits.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+struct AddOp {
+    static __device__ __forceinline__ float apply(float a, float b) { return a + b; }
+    static constexpr float identity() { return 0.0f; }
+};
+struct MaxOp {
+    static __device__ __forceinline__ float apply(float a, float b) { return fmaxf(a, b); }
+    static constexpr float identity() { return -INFINITY; }
+};
+
+template <class R>
+__device__ __forceinline__ float wave_allreduce(float v) {
+    v = R::apply(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = R::apply(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = R::apply(v, dpp_mov<0x141>(v));  // row_half_mirror
+    v = R::apply(v, dpp_mov<0x140>(v));  // row_mirror
+    const unsigned b = __builtin_bit_cast(unsigned, v);
+    auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    v = R::apply(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+    const unsigned c = __builtin_bit_cast(unsigned, v);
+    auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+    v = R::apply(__builtin_bit_cast(float, (unsigned)q[0]), __builtin_bit_cast(float, (unsigned)q[1]));
+    // every lane holds the same value: keep it in a scalar register
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// Reduction over a row team of S wavefronts ("TIRx Metal reduction
+// lowering", section 4.2 protocol): wave collective in every wave, lane 0
+// publishes its wave's partial to LDS, one workgroup barrier, then every wave
+// re-reduces the S partials (identity in the other lanes), so all workers hold
+// the row result with no broadcast barrier.  `slots` is this round's LDS
+// array of Q*S floats; separate rounds use separate arrays, so no second
+// barrier is needed.  S is uniform over the workgroup, so the barrier is
+// reached by every thread or by none.
+template <class R>
+__device__ __forceinline__ float team_reduce(float v, float* slots, int S, const Team& t) {
+    v = wave_allreduce<R>(v);
+    if (S > 1) {
+        if (t.lane == 0) slots[t.q * S + t.s] = v;
+        __syncthreads();
+        const float u = (t.lane < S) ? slots[t.q * S + t.lane] : R::identity();
+        v = wave_allreduce<R>(u);
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Memory access.  Rows are read through their 16-byte aligned grid: a chunk
+// that holds at least one row element lies inside one page of the tensor's
+// allocation, so reading the whole chunk cannot fault even where its other
+// floats belong to a neighbouring row; those floats are replaced by the
+// identity before use and are never written.
+// ---------------------------------------------------------------------------
+// Cache policy.  Every row element is read once and written once, so the
+// row stream carries the nontemporal (streaming) hint on loads and stores;
+// the per-column parameters (gamma, beta) are re-read by every workgroup and
+// use ordinary cached loads.
+#ifndef LR_NT_LOADS
+#define LR_NT_LOADS 1
+#endif
+#ifndef LR_NT_STORES
+#define LR_NT_STORES 1
+#endif
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Row-stream load.
+__device__ __forceinline__ float4 ld4(const float4* p) {
+    if constexpr (LR_NT_LOADS) {
+        const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+
+// Cached load (parameters reused across workgroups).
+__device__ __forceinline__ float4 ld4_cached(const float4* p) { return *p; }
+
+// Row-stream store.
+__device__ __forceinline__ void st4(float4* p, float4 v) {
+    if constexpr (LR_NT_STORES) {
+        v4f w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<v4f*>(p));
+    } else {
+        *p = v;
+    }
+}
+
+__device__ __forceinline__ float get(const float4& v, int j) {
+    return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ void set(float4& v, int j, float f) {
+    if (j == 0) v.x = f; else if (j == 1) v.y = f; else if (j == 2) v.z = f; else v.w = f;
+}
+
+__device__ __forceinline__ float4 splat4(float f) { return make_float4(f, f, f, f); }
+
+// Replace the floats of chunk k that are not row elements by `id`.
+__device__ __forceinline__ void mask_chunk(float4& v, int k, int phase, int cols, float id) {
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        if (!elem_valid(elem_index(k, j, phase), cols)) set(v, j, id);
+    }
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+__device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+}  // namespace lr

@@ -1,0 +1,48 @@
+// Internal interface between the C-ABI layer (lr_abi.cpp), the planner
+// (lr_planner.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "lr.h"
+
+namespace lr {
+
+// Kernel arguments (passed by value).  Unused pointers are null.
+struct KArgs {
+    const float* x;         // input rows (logits for cross-entropy)
+    float* y;               // output rows (softmax, norms)
+    const float* gamma;     // per-column scale or null
+    const float* beta;      // per-column shift or null
+    const int64_t* labels;  // cross-entropy labels
+    float* losses;          // cross-entropy per-row loss
+    int64_t rows;
+    int32_t cols;
+    float eps;
+    float inv_cols;         // 1/cols rounded to FP32 (unordered policy only)
+    int32_t S;              // waves per row
+    int32_t Q;              // rows per workgroup
+    int32_t y_same_phase;   // y rows start at the same 16-byte phase as x rows
+};
+
+// Compiled cache-family chunk counts (chunks_per_lane), ascending.
+constexpr int kCacheChunks[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+constexpr int kNumCacheChunks = sizeof(kCacheChunks) / sizeof(kCacheChunks[0]);
+constexpr int kStreamUnroll = 4;
+
+// Largest workgroup a cache instance is compiled for (launch bounds); the
+// register stripe grows with the chunk count, so the bound shrinks.
+constexpr int cache_max_threads(int nch) { return nch <= 8 ? 1024 : (nch <= 16 ? 512 : 256); }
+
+bool cache_chunks_compiled(int nch);
+
+// Per-op launchers (one translation unit per op).  `aligned` selects the
+// instance for 16-byte aligned rows and parameter vectors.
+hipError_t launch_softmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_rmsnorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_cross_entropy(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_ordered(int op, const KArgs& a, const lr_plan& p, hipStream_t s);
+
+}  // namespace lr

@@ -1,0 +1,398 @@
+// Unordered-policy kernels: the CACHE family (row stripe kept in VGPRs) and
+// the STREAM family (passes reload the row).  Instantiated once per op by
+// the k_<op>.hip translation units.
+//
+// Roles of the steps ("TIRx Metal reduction lowering"):
+//   section 1   softmax: exp(x - max) / sum;  cross-entropy: log(sum) + max - selected
+//   section 4   S waves cooperate on a row, Q rows share a workgroup
+//   section 4.4 blocked-cyclic ownership, V = 4 (one 128-bit access per chunk)
+//   section 5   the row's chunks are kept per worker (here: in VGPRs) so every
+//               pass after the first reads registers, not memory
+//   section 5.1 LayerNorm mean, then variance of the centred values
+//   section 5.2 cross-entropy reads logits[row, label] from the global tensor
+//               under a 0 <= label < cols guard (fill 0)
+#pragma once
+
+#include "lr_device.hpp"
+#include "lr_internal.hpp"
+
+namespace lr {
+
+template <int OP>
+constexpr float op_identity() {
+    return (OP == kSoftmax || OP == kCrossEntropy) ? -INFINITY : 0.0f;
+}
+
+// Reads label[row] and the guarded logit once per row (worker 0 of the team).
+__device__ __forceinline__ float gather_label(const KArgs& a, const float* xr, int64_t row) {
+    const int64_t lab = a.labels[row];
+    return (lab >= 0 && lab < (int64_t)a.cols) ? xr[lab] : 0.0f;
+}
+
+// Stores out, the values of chunk k of row yr (x-row phase h).
+template <bool AL>
+__device__ __forceinline__ void store_chunk(const KArgs& a, float* yr, int k, int h, float4 out) {
+    if (AL) {
+        st4(reinterpret_cast<float4*>(yr) + k, out);
+    } else if (a.y_same_phase && chunk_full(k, h, a.cols)) {
+        st4(reinterpret_cast<float4*>(yr - h) + k, out);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int e = elem_index(k, j, h);
+            if (elem_valid(e, a.cols)) yr[e] = get(out, j);
+        }
+    }
+}
+
+// Per-column parameter (gamma or beta) for chunk k; `fill` where absent.
+template <bool AL>
+__device__ __forceinline__ float4 param_chunk(const float* p, int k, int h, int cols, float fill) {
+    if (p == nullptr) return splat4(fill);
+    if (AL) return ld4_cached(reinterpret_cast<const float4*>(p) + k);
+    float4 g;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        const int e = elem_index(k, j, h);
+        set(g, j, elem_valid(e, cols) ? p[e] : fill);
+    }
+    return g;
+}
+
+// Aligned rows: chunk k of a parameter vector loaded without a branch.  An
+// absent parameter reads the row instead (a valid address) and returns
+// `fill`, so the load phase is straight-line code.
+__device__ __forceinline__ float4 param_chunk_aligned(const float* p, const float* any_valid, int k,
+                                                      float fill) {
+    const float4 raw = ld4_cached(reinterpret_cast<const float4*>(p ? p : any_valid) + k);
+    return p ? raw : splat4(fill);
+}
+
+// ===========================================================================
+// CACHE family: worker w keeps chunks k = w + W*c, c < NCH, in registers.
+// ===========================================================================
+template <int OP, int NCH, bool AL>
+__global__ void __launch_bounds__(cache_max_threads(NCH))
+k_cache(const KArgs a) {
+    __shared__ float red[2][kMaxWaves];
+    constexpr float ID = op_identity<OP>();
+    // parameter chunks held in registers early (bounded so the stripe does not spill)
+    constexpr bool kPrefetch = (OP == kLayerNorm) ? NCH <= 6 : NCH <= 8;
+    const int S = a.S;
+    const int W = kWave * S;
+    const Team t = team_of((int)threadIdx.x, S);
+    const int64_t row = row_of(blockIdx.x, a.Q, t.q);
+    const bool active = row < a.rows;
+    const int cols = a.cols;
+    const float* xr = a.x + (active ? row : 0) * (int64_t)cols;
+    const int h = AL ? 0 : phase_of(reinterpret_cast<uintptr_t>(xr));
+    const int nv = active ? (AL ? cols / kVec : chunks_of(h, cols)) : 0;
+    const float4* xa = reinterpret_cast<const float4*>(xr - h);
+
+    // Every load is issued unconditionally (straight-line code, so each wait
+    // covers only the loads it needs): a slot past the row's last chunk
+    // re-reads that last chunk -- always a valid address; an inactive team
+    // reads the tensor's first chunk -- and then takes the identity instead.
+    const int klast = (nv > 0 ? nv : 1) - 1;
+    float4 v[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int k = chunk_index(t.w, W, c);
+        const float4 raw = ld4(xa + min(k, klast));
+        v[c] = (k < nv) ? raw : splat4(ID);
+        if (!AL) mask_chunk(v[c], k, h, cols, ID);
+    }
+
+    float sel = 0.0f;
+    if constexpr (OP == kCrossEntropy) {
+        if (active && t.w == 0) sel = gather_label(a, xr, row);
+    }
+
+    if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
+        float m = ID;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            m = fmaxf(fmaxf(m, fmaxf(v[c].x, v[c].y)), fmaxf(v[c].z, v[c].w));
+        m = team_reduce<MaxOp>(m, red[0], S, t);
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            v[c].x = fast_exp(v[c].x - m);
+            v[c].y = fast_exp(v[c].y - m);
+            v[c].z = fast_exp(v[c].z - m);
+            v[c].w = fast_exp(v[c].w - m);
+            s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+        }
+        s = team_reduce<AddOp>(s, red[1], S, t);
+        if constexpr (OP == kCrossEntropy) {
+            if (active && t.w == 0) a.losses[row] = (fast_log(s) + m) - sel;
+        } else {
+            const float r = fast_rcp(s);
+            float* yr = a.y + row * (int64_t)cols;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int k = chunk_index(t.w, W, c);
+                if (k < nv) {
+                    const float4 o = make_float4(v[c].x * r, v[c].y * r, v[c].z * r, v[c].w * r);
+                    store_chunk<AL>(a, yr, k, h, o);
+                }
+            }
+        }
+    } else if constexpr (OP == kRmsNorm) {
+        // short stripes: fetch gamma now so its latency hides behind the reduction
+        float4 gp[kPrefetch ? NCH : 1];
+        if constexpr (kPrefetch) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int k = chunk_index(t.w, W, c);
+                gp[c] = AL ? param_chunk_aligned(a.gamma, xr, min(k, klast), 1.0f)
+                           : param_chunk<AL>(a.gamma, min(k, klast), h, cols, 1.0f);
+            }
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            ss += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
+        ss = team_reduce<AddOp>(ss, red[0], S, t);
+        const float r = fast_rsqrt(ss * a.inv_cols + a.eps);
+        float* yr = a.y + row * (int64_t)cols;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int k = chunk_index(t.w, W, c);
+            if (k < nv) {
+                const float4 g = kPrefetch ? gp[c] : param_chunk<AL>(a.gamma, k, h, cols, 1.0f);
+                const float4 o = make_float4(v[c].x * r * g.x, v[c].y * r * g.y,
+                                             v[c].z * r * g.z, v[c].w * r * g.w);
+                store_chunk<AL>(a, yr, k, h, o);
+            }
+        }
+    } else {  // kLayerNorm
+        float4 gp[kPrefetch ? NCH : 1], bp[kPrefetch ? NCH : 1];
+        if constexpr (kPrefetch) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int k = chunk_index(t.w, W, c);
+                gp[c] = AL ? param_chunk_aligned(a.gamma, xr, min(k, klast), 1.0f)
+                           : param_chunk<AL>(a.gamma, min(k, klast), h, cols, 1.0f);
+                bp[c] = AL ? param_chunk_aligned(a.beta, xr, min(k, klast), 0.0f)
+                           : param_chunk<AL>(a.beta, min(k, klast), h, cols, 0.0f);
+            }
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) sum += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+        sum = team_reduce<AddOp>(sum, red[0], S, t);
+        const float mu = sum * a.inv_cols;
+        float qs = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int k = chunk_index(t.w, W, c);
+            float4 d = make_float4(v[c].x - mu, v[c].y - mu, v[c].z - mu, v[c].w - mu);
+            if (k >= nv) d = splat4(0.0f);
+            if (!AL) mask_chunk(d, k, h, cols, 0.0f);
+            v[c] = d;
+            qs += (d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w);
+        }
+        qs = team_reduce<AddOp>(qs, red[1], S, t);
+        const float r = fast_rsqrt(qs * a.inv_cols + a.eps);
+        float* yr = a.y + row * (int64_t)cols;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int k = chunk_index(t.w, W, c);
+            if (k < nv) {
+                const float4 g = kPrefetch ? gp[c] : param_chunk<AL>(a.gamma, k, h, cols, 1.0f);
+                const float4 b = kPrefetch ? bp[c] : param_chunk<AL>(a.beta, k, h, cols, 0.0f);
+                const float4 o = make_float4(v[c].x * r * g.x + b.x, v[c].y * r * g.y + b.y,
+                                             v[c].z * r * g.z + b.z, v[c].w * r * g.w + b.w);
+                store_chunk<AL>(a, yr, k, h, o);
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// STREAM family: the row is walked in trips of U chunks per worker; passes
+// that need it again reload it.  Softmax and cross-entropy fold (max,
+// sum of exp) online in one pass and merge the per-worker pairs at the end.
+// ===========================================================================
+template <int OP, bool AL>
+__device__ __forceinline__ void load_trip(float4 (&v)[kStreamUnroll], const float4* xa, int k0,
+                                          int W, int nv, int h, int cols, float id) {
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+        const int k = k0 + W * u;
+        v[u] = (k < nv) ? ld4(xa + k) : splat4(id);
+        if (!AL) mask_chunk(v[u], k, h, cols, id);
+    }
+}
+
+template <int OP, bool AL>
+__global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
+    __shared__ float red[2][kMaxWaves];
+    constexpr int U = kStreamUnroll;
+    constexpr float ID = op_identity<OP>();
+    const int S = a.S;
+    const int W = kWave * S;
+    const Team t = team_of((int)threadIdx.x, S);
+    const int64_t row = row_of(blockIdx.x, a.Q, t.q);
+    const bool active = row < a.rows;
+    const int cols = a.cols;
+    const float* xr = a.x + (active ? row : 0) * (int64_t)cols;
+    const int h = AL ? 0 : phase_of(reinterpret_cast<uintptr_t>(xr));
+    const int nv = active ? (AL ? cols / kVec : chunks_of(h, cols)) : 0;
+    const float4* xa = reinterpret_cast<const float4*>(xr - h);
+    float* yr = a.y + (active ? row : 0) * (int64_t)cols;
+
+    float sel = 0.0f;
+    if constexpr (OP == kCrossEntropy) {
+        if (active && t.w == 0) sel = gather_label(a, xr, row);
+    }
+
+    if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
+        float m = -INFINITY, s = 0.0f;
+        for (int k0 = t.w; k0 < nv; k0 += W * U) {
+            float4 v[U];
+            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+            float tm = m;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                tm = fmaxf(fmaxf(tm, fmaxf(v[u].x, v[u].y)), fmaxf(v[u].z, v[u].w));
+            s *= fast_exp(m - tm);  // m = -inf on the first trip: s is 0 anyway
+            m = tm;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                s += (fast_exp(v[u].x - m) + fast_exp(v[u].y - m)) +
+                     (fast_exp(v[u].z - m) + fast_exp(v[u].w - m));
+        }
+        const float M = team_reduce<MaxOp>(m, red[0], S, t);
+        // a worker with no elements has m = -inf and s = 0
+        const float sc = (m == -INFINITY) ? 0.0f : s * fast_exp(m - M);
+        const float tot = team_reduce<AddOp>(sc, red[1], S, t);
+        if constexpr (OP == kCrossEntropy) {
+            if (active && t.w == 0) a.losses[row] = (fast_log(tot) + M) - sel;
+        } else {
+            const float r = fast_rcp(tot);
+            for (int k0 = t.w; k0 < nv; k0 += W * U) {
+                float4 v[U];
+                load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int k = k0 + W * u;
+                    if (k < nv) {
+                        const float4 o = make_float4(fast_exp(v[u].x - M) * r, fast_exp(v[u].y - M) * r,
+                                                     fast_exp(v[u].z - M) * r, fast_exp(v[u].w - M) * r);
+                        store_chunk<AL>(a, yr, k, h, o);
+                    }
+                }
+            }
+        }
+    } else if constexpr (OP == kRmsNorm) {
+        float ss = 0.0f;
+        for (int k0 = t.w; k0 < nv; k0 += W * U) {
+            float4 v[U];
+            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                ss += (v[u].x * v[u].x + v[u].y * v[u].y) + (v[u].z * v[u].z + v[u].w * v[u].w);
+        }
+        ss = team_reduce<AddOp>(ss, red[0], S, t);
+        const float r = fast_rsqrt(ss * a.inv_cols + a.eps);
+        for (int k0 = t.w; k0 < nv; k0 += W * U) {
+            float4 v[U];
+            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + W * u;
+                if (k < nv) {
+                    const float4 g = param_chunk<AL>(a.gamma, k, h, cols, 1.0f);
+                    const float4 o = make_float4(v[u].x * r * g.x, v[u].y * r * g.y,
+                                                 v[u].z * r * g.z, v[u].w * r * g.w);
+                    store_chunk<AL>(a, yr, k, h, o);
+                }
+            }
+        }
+    } else {  // kLayerNorm
+        float sum = 0.0f;
+        for (int k0 = t.w; k0 < nv; k0 += W * U) {
+            float4 v[U];
+            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+#pragma unroll
+            for (int u = 0; u < U; ++u) sum += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+        }
+        sum = team_reduce<AddOp>(sum, red[0], S, t);
+        const float mu = sum * a.inv_cols;
+        float qs = 0.0f;
+        for (int k0 = t.w; k0 < nv; k0 += W * U) {
+            float4 v[U];
+            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + W * u;
+                float4 d = make_float4(v[u].x - mu, v[u].y - mu, v[u].z - mu, v[u].w - mu);
+                if (k >= nv) d = splat4(0.0f);
+                if (!AL) mask_chunk(d, k, h, cols, 0.0f);
+                qs += (d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w);
+            }
+        }
+        qs = team_reduce<AddOp>(qs, red[1], S, t);
+        const float r = fast_rsqrt(qs * a.inv_cols + a.eps);
+        for (int k0 = t.w; k0 < nv; k0 += W * U) {
+            float4 v[U];
+            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + W * u;
+                if (k < nv) {
+                    const float4 g = param_chunk<AL>(a.gamma, k, h, cols, 1.0f);
+                    const float4 b = param_chunk<AL>(a.beta, k, h, cols, 0.0f);
+                    const float4 o = make_float4((v[u].x - mu) * r * g.x + b.x, (v[u].y - mu) * r * g.y + b.y,
+                                                 (v[u].z - mu) * r * g.z + b.z, (v[u].w - mu) * r * g.w + b.w);
+                    store_chunk<AL>(a, yr, k, h, o);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch by plan: selects the compiled instance and launches it on `s`.
+// ---------------------------------------------------------------------------
+template <int OP, int NCH, bool AL>
+hipError_t launch_cache_inst(const KArgs& a, const lr_plan& p, hipStream_t s) {
+    hipLaunchKernelGGL((k_cache<OP, NCH, AL>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int OP, bool AL>
+hipError_t launch_cache_al(const KArgs& a, const lr_plan& p, hipStream_t s) {
+    switch (p.chunks_per_lane) {
+        case 1: return launch_cache_inst<OP, 1, AL>(a, p, s);
+        case 2: return launch_cache_inst<OP, 2, AL>(a, p, s);
+        case 3: return launch_cache_inst<OP, 3, AL>(a, p, s);
+        case 4: return launch_cache_inst<OP, 4, AL>(a, p, s);
+        case 6: return launch_cache_inst<OP, 6, AL>(a, p, s);
+        case 8: return launch_cache_inst<OP, 8, AL>(a, p, s);
+        case 12: return launch_cache_inst<OP, 12, AL>(a, p, s);
+        case 16: return launch_cache_inst<OP, 16, AL>(a, p, s);
+        case 24: return launch_cache_inst<OP, 24, AL>(a, p, s);
+        case 32: return launch_cache_inst<OP, 32, AL>(a, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OP>
+hipError_t launch_op(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s) {
+    if (p.family == LR_FAMILY_CACHE) {
+        return aligned ? launch_cache_al<OP, true>(a, p, s) : launch_cache_al<OP, false>(a, p, s);
+    }
+    if (p.family == LR_FAMILY_STREAM) {
+        if (aligned)
+            hipLaunchKernelGGL((k_stream<OP, true>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream<OP, false>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lr

@@ -1,0 +1,69 @@
+// Thread -> (row, element) mapping shared by the kernels and the host
+// coverage replay (lr_coverage_check), so that the replay checks the very
+// functions the kernels are built from.
+//
+// Mapping algebra of "TIRx Metal reduction lowering", section 4, re-derived
+// for 64-lane wavefronts:  W = 64*S workers cooperate on one row, a
+// workgroup packs Q rows (64*S*Q threads), worker w owns the 16-byte chunks
+// k = w + W*c (blocked-cyclic ownership with V = 4, section 4.4), and a chunk
+// covers the four consecutive floats 4k .. 4k+3 of the row's 16-byte aligned
+// grid.  A row that does not start on a 16-byte boundary sits `phase`
+// floats into its first chunk; grid slots outside [0, cols) are not
+// elements of the row and take the reduction identity.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define LR_HD __host__ __device__ __forceinline__
+#else
+#define LR_HD inline
+#endif
+
+namespace lr {
+
+constexpr int kWave = 64;       // lanes per wavefront (gfx950)
+constexpr int kVec = 4;         // floats per 128-bit chunk
+constexpr int kMaxWaves = 16;   // 1024 threads per workgroup
+constexpr int kSlab = 256;      // ordered family: floats folded per LDS slab
+
+struct Team {
+    int q;     // packed row within the workgroup
+    int w;     // worker within the row team, 0 .. 64*S-1
+    int s;     // wavefront within the row team
+    int lane;  // lane within the wavefront
+};
+
+LR_HD Team team_of(int tid, int S) {
+    const int W = kWave * S;
+    const int q = tid / W;
+    const int w = tid - q * W;
+    return Team{q, w, w / kWave, tid % kWave};
+}
+
+LR_HD int64_t row_of(int64_t block, int Q, int q) { return block * Q + q; }
+
+// Floats between the 16-byte boundary at or below `addr` and `addr`.
+LR_HD int phase_of(uintptr_t addr) { return (int)((addr & 15u) >> 2); }
+
+// 16-byte chunks of the aligned grid that touch a row of `cols` floats.
+LR_HD int chunks_of(int phase, int cols) { return (phase + cols + kVec - 1) / kVec; }
+
+// Chunk owned by worker w at stripe slot c.
+LR_HD int chunk_index(int w, int W, int c) { return w + W * c; }
+
+// Row element held in float j of chunk k (may fall outside [0, cols)).
+LR_HD int elem_index(int k, int j, int phase) { return kVec * k + j - phase; }
+
+LR_HD bool elem_valid(int e, int cols) { return (unsigned)e < (unsigned)cols; }
+
+// Chunk k holds four row elements (no guard needed for it).
+LR_HD bool chunk_full(int k, int phase, int cols) {
+    return kVec * k - phase >= 0 && kVec * k + kVec - phase <= cols;
+}
+
+// Ordered family: one wavefront per row; lane l loads element
+// kSlab*slab + 64*i + l, i = 0..3, into slot 64*i + l of its LDS slab.
+LR_HD int ordered_elem(int slab, int i, int lane) { return kSlab * slab + kWave * i + lane; }
+
+}  // namespace lr

@@ -1,0 +1,278 @@
+// Host planner: legal-plan enumeration, the MI355X prior that picks the
+// automatic plan, validation of explicit plans, and the host replay of a
+// plan's thread -> element mapping.
+//
+// Follows the solver structure of "TIRx Metal reduction lowering", section 6:
+// legality is decided first (hard device limits and the register-stripe
+// budget), the finite candidate set is enumerated exhaustively, a prior
+// ranks the survivors, and an explicit plan is honoured exactly or rejected,
+// never clamped.  The Metal cost prior itself is not used; the MI355X prior
+// below is this library's own (wave64, 256 CUs x 4 SIMDs, VGPR-resident
+// stripes), and measured plan choices for known shapes live in
+// lr_plan_table.inc.
+#include <algorithm>
+#include <climits>
+#include <cstring>
+
+#include "lr_internal.hpp"
+#include "lr_map.hpp"
+
+namespace lr {
+
+bool cache_chunks_compiled(int nch) {
+    for (int i = 0; i < kNumCacheChunks; ++i)
+        if (kCacheChunks[i] == nch) return true;
+    return false;
+}
+
+// 16-byte chunks a worker must reach for the widest row of the problem.
+static int64_t max_row_chunks(int64_t cols, bool aligned) {
+    return aligned ? cols / kVec : (cols + 3 + kVec - 1) / kVec;  // phase up to 3
+}
+
+static int reductions_of(int op) {
+    return op == LR_OP_RMSNORM ? 1 : 2;
+}
+
+static int smallest_cache_instance(int64_t need) {
+    for (int i = 0; i < kNumCacheChunks; ++i)
+        if (kCacheChunks[i] >= need) return kCacheChunks[i];
+    return 0;
+}
+
+static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_t cols, int op, bool aligned) {
+    lr_plan p;
+    std::memset(&p, 0, sizeof(p));
+    p.family = family;
+    p.waves_per_row = S;
+    p.rows_per_block = Q;
+    p.vec = family == LR_FAMILY_ORDERED ? 1 : kVec;
+    p.chunks_per_lane = nch;
+    p.threads_per_block = kWave * S * Q;
+    p.blocks = (rows + Q - 1) / Q;
+    p.reductions = reductions_of(op);
+    p.lds_bytes = family == LR_FAMILY_ORDERED ? Q * kSlab * 4 : 2 * kMaxWaves * 4;
+    p.row_aligned = aligned ? 1 : 0;
+    return p;
+}
+
+static bool valid_op(int op) { return op >= LR_OP_SOFTMAX && op <= LR_OP_CROSS_ENTROPY; }
+static bool valid_policy(int p) { return p == LR_UNORDERED_TREE || p == LR_ORDERED_FOLD; }
+
+static lr_status check_problem(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy) {
+    if (f == nullptr) return LR_ERR_NULL_POINTER;
+    if (!valid_op(op)) return LR_ERR_INVALID_ARGUMENT;
+    if (!valid_policy(policy)) return LR_ERR_INVALID_POLICY;
+    if (rows < 0 || cols < 1 || cols >= (int64_t(1) << 24) || rows > INT32_MAX) return LR_ERR_INVALID_SHAPE;
+    if (f->compute_units < 1 || f->max_threads_per_block < kWave || f->wave_size != kWave)
+        return LR_ERR_INVALID_ARGUMENT;
+    return LR_OK;
+}
+
+lr_status validate_plan(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy,
+                        bool aligned, const lr_plan* p) {
+    lr_status st = check_problem(f, op, rows, cols, policy);
+    if (st != LR_OK) return st;
+    if (p == nullptr) return LR_ERR_NULL_POINTER;
+    const int S = p->waves_per_row, Q = p->rows_per_block;
+    if (S < 1 || Q < 1 || S > kMaxWaves || Q > kMaxWaves || S * Q > kMaxWaves) return LR_ERR_UNREALIZABLE_PLAN;
+    if (p->threads_per_block != kWave * S * Q || p->threads_per_block > f->max_threads_per_block)
+        return LR_ERR_UNREALIZABLE_PLAN;
+    const int64_t blocks = (rows + Q - 1) / Q;
+    if (p->blocks != blocks || blocks > INT32_MAX) return LR_ERR_UNREALIZABLE_PLAN;
+    const bool ordered = policy == LR_ORDERED_FOLD;
+    if (ordered != (p->family == LR_FAMILY_ORDERED)) return LR_ERR_UNREALIZABLE_PLAN;
+    switch (p->family) {
+        case LR_FAMILY_CACHE: {
+            if (p->vec != kVec || !cache_chunks_compiled(p->chunks_per_lane)) return LR_ERR_UNREALIZABLE_PLAN;
+            const int64_t need = (max_row_chunks(cols, aligned) + kWave * S - 1) / (kWave * S);
+            if (p->chunks_per_lane < need) return LR_ERR_UNREALIZABLE_PLAN;
+            if (p->threads_per_block > cache_max_threads(p->chunks_per_lane)) return LR_ERR_UNREALIZABLE_PLAN;
+            return LR_OK;
+        }
+        case LR_FAMILY_STREAM:
+            if (p->vec != kVec || p->chunks_per_lane != kStreamUnroll) return LR_ERR_UNREALIZABLE_PLAN;
+            return LR_OK;
+        case LR_FAMILY_ORDERED:
+            if (S != 1 || p->vec != 1 || p->chunks_per_lane != 0) return LR_ERR_UNREALIZABLE_PLAN;
+            return LR_OK;
+        default:
+            return LR_ERR_UNREALIZABLE_PLAN;
+    }
+}
+
+// All legal plans in enumeration order: family, then S, then Q.
+static int enumerate_all(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy,
+                         bool aligned, lr_plan* out, int cap) {
+    int n = 0;
+    auto push = [&](const lr_plan& p) {
+        if (validate_plan(f, op, rows, cols, policy, aligned, &p) != LR_OK) return;
+        if (out != nullptr && n < cap) out[n] = p;
+        ++n;
+    };
+    if (policy == LR_ORDERED_FOLD) {
+        for (int Q = 1; Q <= kMaxWaves; ++Q) push(make_plan(LR_FAMILY_ORDERED, 1, Q, 0, rows, cols, op, aligned));
+        return n;
+    }
+    const int64_t nv = max_row_chunks(cols, aligned);
+    for (int S = 1; S <= kMaxWaves; ++S) {
+        const int64_t need = (nv + kWave * S - 1) / (kWave * S);
+        const int nch = smallest_cache_instance(need);
+        if (nch == 0) continue;
+        for (int Q = 1; S * Q <= kMaxWaves; ++Q) push(make_plan(LR_FAMILY_CACHE, S, Q, nch, rows, cols, op, aligned));
+    }
+    for (int S = 1; S <= kMaxWaves; ++S)
+        for (int Q = 1; S * Q <= kMaxWaves; ++Q)
+            push(make_plan(LR_FAMILY_STREAM, S, Q, kStreamUnroll, rows, cols, op, aligned));
+    return n;
+}
+
+// ---------------------------------------------------------------------------
+// MI355X prior.  Rows are independent and the kernels are HBM-bound, so the
+// plan's job is to keep enough 128-bit loads in flight on every CU while
+// keeping the register stripe short:
+//   * enough wavefronts: the smallest S with rows*S >= 2 waves per SIMD of
+//     the device, so few-row problems spread each row over more waves;
+//   * register budget: widen S until the stripe is <= 8 chunks (32 floats)
+//     per lane -- short stripes keep occupancy high and leave registers for
+//     the gamma/beta prefetch;
+//   * cross-entropy keeps nothing after its single pass, so long rows take
+//     the STREAM family (online max / sum of exp, no register copy);
+//   * one row per workgroup, except that single-wave rows are packed four to
+//     a workgroup when rows are plentiful.
+// Measured winners for known shapes (lr_plan_table.inc) take precedence.
+// ---------------------------------------------------------------------------
+struct TableEntry {
+    int op;
+    int policy;
+    int64_t rows;
+    int64_t cols;
+    int aligned;
+    int family, S, Q, nch;
+};
+
+static const TableEntry kTable[] = {
+#include "lr_plan_table.inc"
+};
+
+static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy,
+                          bool aligned) {
+    for (const TableEntry& e : kTable) {
+        if (e.op == op && e.policy == policy && e.rows == rows && e.cols == cols &&
+            e.aligned == (aligned ? 1 : 0)) {
+            lr_plan p = make_plan(e.family, e.S, e.Q, e.nch, rows, cols, op, aligned);
+            if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
+        }
+    }
+    const int64_t simds = (int64_t)f->compute_units * (f->simds_per_cu > 0 ? f->simds_per_cu : 4);
+    if (policy == LR_ORDERED_FOLD) {
+        const int Q = rows >= 4 * simds ? 4 : 1;
+        return make_plan(LR_FAMILY_ORDERED, 1, Q, 0, rows, cols, op, aligned);
+    }
+    const int64_t nv = max_row_chunks(cols, aligned);
+    const int64_t target_waves = 2 * simds;
+    auto need = [&](int s) { return (nv + kWave * s - 1) / (kWave * s); };
+    int S = 1;
+    while (S < kMaxWaves && (int64_t)rows * S < target_waves) ++S;
+    while (S < kMaxWaves && need(S) > 8) ++S;
+    int family = LR_FAMILY_CACHE;
+    int nch = smallest_cache_instance(need(S));
+    if (nch == 0 || (op == LR_OP_CROSS_ENTROPY && need(S) > 8)) {
+        family = LR_FAMILY_STREAM;
+        nch = kStreamUnroll;
+        if (op == LR_OP_CROSS_ENTROPY) S = std::max(S, 8);
+    }
+    int Q = (S == 1 && rows >= 4 * (int64_t)f->compute_units * 4) ? 4 : 1;
+    lr_plan p = make_plan(family, S, Q, nch, rows, cols, op, aligned);
+    if (validate_plan(f, op, rows, cols, policy, aligned, &p) != LR_OK)
+        p = make_plan(LR_FAMILY_STREAM, S, 1, kStreamUnroll, rows, cols, op, aligned);
+    return p;
+}
+
+}  // namespace lr
+
+using namespace lr;
+
+extern "C" void lr_device_facts_mi355x(lr_device_facts* out) {
+    if (out == nullptr) return;
+    out->compute_units = 256;
+    out->max_threads_per_block = 1024;
+    out->simds_per_cu = 4;
+    out->wave_size = 64;
+}
+
+extern "C" lr_status lr_plan_for_device(const lr_device_facts* facts, lr_op op, int64_t rows, int64_t cols,
+                                        lr_reduction_policy policy, int32_t row_aligned, lr_plan* out) {
+    lr_status st = check_problem(facts, op, rows, cols, policy);
+    if (st != LR_OK) return st;
+    if (out == nullptr) return LR_ERR_NULL_POINTER;
+    const bool aligned = row_aligned != 0 && cols % kVec == 0;
+    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned);
+    st = validate_plan(facts, op, rows, cols, policy, aligned, &p);
+    if (st != LR_OK) return st;
+    *out = p;
+    return LR_OK;
+}
+
+extern "C" lr_status lr_plan_enumerate(const lr_device_facts* facts, lr_op op, int64_t rows, int64_t cols,
+                                       lr_reduction_policy policy, int32_t row_aligned, lr_plan* out,
+                                       int32_t capacity, int32_t* count) {
+    lr_status st = check_problem(facts, op, rows, cols, policy);
+    if (st != LR_OK) return st;
+    if (count == nullptr || capacity < 0 || (out == nullptr && capacity > 0)) return LR_ERR_NULL_POINTER;
+    const bool aligned = row_aligned != 0 && cols % kVec == 0;
+    *count = enumerate_all(facts, op, rows, cols, policy, aligned, out, capacity);
+    return LR_OK;
+}
+
+extern "C" lr_status lr_plan_validate(const lr_device_facts* facts, lr_op op, int64_t rows, int64_t cols,
+                                      lr_reduction_policy policy, int32_t row_aligned, const lr_plan* plan) {
+    const bool aligned = row_aligned != 0 && cols % kVec == 0;
+    return validate_plan(facts, op, rows, cols, policy, aligned, plan);
+}
+
+extern "C" lr_status lr_coverage_check(const lr_plan* p, int64_t rows, int64_t cols, int32_t phase,
+                                       uint32_t* counts) {
+    if (p == nullptr || counts == nullptr) return LR_ERR_NULL_POINTER;
+    if (rows < 0 || cols < 1 || cols >= (int64_t(1) << 24)) return LR_ERR_INVALID_SHAPE;
+    if (phase < 0 || phase > 3) return LR_ERR_INVALID_ARGUMENT;
+    const int S = p->waves_per_row, Q = p->rows_per_block;
+    if (S < 1 || Q < 1 || p->threads_per_block != kWave * S * Q) return LR_ERR_UNREALIZABLE_PLAN;
+    const int c = (int)cols;
+    for (int64_t b = 0; b < p->blocks; ++b) {
+        for (int tid = 0; tid < p->threads_per_block; ++tid) {
+            if (p->family == LR_FAMILY_ORDERED) {
+                const int lane = tid % kWave, wave = tid / kWave;
+                const int64_t row = row_of(b, Q, wave);
+                if (row >= rows) continue;
+                for (int slab = 0; slab * kSlab < c; ++slab)
+                    for (int i = 0; i < kSlab / kWave; ++i) {
+                        const int e = ordered_elem(slab, i, lane);
+                        if (e < c) counts[row * cols + e] += 1;
+                    }
+                continue;
+            }
+            const Team t = team_of(tid, S);
+            const int W = kWave * S;
+            const int64_t row = row_of(b, Q, t.q);
+            if (row >= rows) continue;
+            const int h = (int)((phase + (row * cols) % kVec) % kVec);
+            const int nv = chunks_of(h, c);
+            auto visit = [&](int k) {
+                if (k >= nv) return;
+                for (int j = 0; j < kVec; ++j) {
+                    const int e = elem_index(k, j, h);
+                    if (elem_valid(e, c)) counts[row * cols + e] += 1;
+                }
+            };
+            if (p->family == LR_FAMILY_CACHE) {
+                for (int cc = 0; cc < p->chunks_per_lane; ++cc) visit(chunk_index(t.w, W, cc));
+            } else {
+                const int U = p->chunks_per_lane;
+                for (int k0 = t.w; k0 < nv; k0 += W * U)
+                    for (int u = 0; u < U; ++u) visit(k0 + W * u);
+            }
+        }
+    }
+    return LR_OK;
+}

@@ -1,0 +1,127 @@
+"""HBM traffic from rocprofv3 counter runs, tied to the kernel sources.
+
+Two `rocprofv3 --pmc` runs of the benchmark (one with FETCH_SIZE, one with
+WRITE_SIZE, both launched with `bench.py --copy-probe`) give KiB per
+dispatch for every kernel.  The counters are calibrated against a plain
+device-to-device copy of known size that runs in the same process (the last
+20 `__amd_rocclr_copyBuffer` dispatches): bytes = counter * (known bytes /
+copy's counter).  The summary records a hash of the HIP sources, so a figure
+taken before a kernel change is not reported for the changed kernel.
+
+    python -m row_reductions_amd.profiling traffic --fetch F.csv --write W.csv \\
+        --copy-bytes 18874368 --out profiles/hbm_traffic_768x6144.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+OP_NAMES = {0: "softmax", 1: "rmsnorm", 2: "layernorm", 3: "cross_entropy"}
+
+
+def csrc_hash() -> str:
+    """sha256 over the library's HIP/C++ sources (names and contents)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".inc", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def _per_kernel(path: str):
+    vals = defaultdict(list)
+    order = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+            order.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return vals, order
+
+
+def kernel_op(name: str):
+    m = re.search(r"lr::k_(cache|stream|ordered)<(\d+)", name)
+    return OP_NAMES.get(int(m.group(2))) if m else None
+
+
+def traffic(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
+    out = {"csrc_sha256": csrc_hash(), "copy_bytes": copy_bytes, "kernels": {}}
+    scale = {}
+    per = {}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        vals, order = _per_kernel(path)
+        probe = [v for n, v in order if "copyBuffer" in n][-20:]
+        if not probe:
+            raise SystemExit(f"{path}: no copy probe dispatches")
+        copy_kib = sum(probe) / len(probe)
+        scale[key] = copy_bytes / (copy_kib * 1024.0)
+        out[f"copy_{key}_kib"] = copy_kib
+        out[f"{key}_scale"] = scale[key]
+        per[key] = vals
+    for name in per["fetch"]:
+        op = kernel_op(name)
+        if op is None or name not in per["write"]:
+            continue
+        f_kib = sum(per["fetch"][name]) / len(per["fetch"][name])
+        w_kib = sum(per["write"][name]) / len(per["write"][name])
+        out["kernels"][name] = {
+            "op": op,
+            "fetch_kib": f_kib,
+            "write_kib": w_kib,
+            "fetch_bytes": f_kib * 1024.0 * scale["fetch"],
+            "write_bytes": w_kib * 1024.0 * scale["write"],
+            "traffic_bytes": f_kib * 1024.0 * scale["fetch"] + w_kib * 1024.0 * scale["write"],
+            "dispatches": len(per["fetch"][name]),
+        }
+    return out
+
+
+def lookup(summary_path: str, op: str):
+    """Traffic record of `op` if the summary matches the current sources."""
+    try:
+        with open(summary_path) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if s.get("csrc_sha256") != csrc_hash():
+        return None
+    for name, rec in s.get("kernels", {}).items():
+        if rec.get("op") == op:
+            return dict(rec, kernel=name)
+    return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--command", default="", help="the profiling command, recorded in the summary")
+    t.add_argument("--out", required=True)
+    sub.add_parser("hash")
+    a = ap.parse_args(argv)
+    if a.cmd == "hash":
+        print(csrc_hash())
+        return 0
+    s = traffic(a.fetch, a.write, a.copy_bytes)
+    s["command"] = a.command
+    with open(a.out, "w") as f:
+        json.dump(s, f, indent=1)
+    for name, rec in s["kernels"].items():
+        print(f"{rec['op']:14s} fetch {rec['fetch_bytes'] / 1e6:8.2f} MB  write {rec['write_bytes'] / 1e6:8.2f} MB  "
+              f"{name}")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

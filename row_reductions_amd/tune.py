@@ -1,0 +1,125 @@
+"""Measured plan selection for one problem shape (staged tuning).
+
+Follows the authority split of "TIRx Metal reduction lowering", section 7:
+legality comes from the planner (every candidate is a legal plan of
+lr_plan_enumerate), and the fastest *valid* candidate, measured on the
+device, is the winner.  Each candidate's output is checked against the
+automatic plan's output (|a - b| <= 1e-6 + 1e-5 |b|); a candidate that fails
+is reported and never selected.  The winner is re-measured before it is
+printed as a line for lr_plan_table.inc.
+
+    python -m row_reductions_amd.tune --op layernorm --rows 768 --cols 6144
+
+Timing: `--sets` rotating input/output buffer sets (cold cache by default),
+`--iters` back-to-back launches on one stream between two HIP events.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+
+import torch
+
+import row_reductions_amd as lr
+
+
+def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh):
+    pol = lr._policy(policy)
+
+    def run(i, plan):
+        k = i % len(xs)
+        if op == "softmax":
+            return lr.lr_softmax_f32(xs[k], ys[k], rows, cols, pol, sh, plan)
+        if op == "rmsnorm":
+            return lr.lr_rmsnorm_f32(xs[k], g, ys[k], rows, cols, eps, pol, sh, plan)
+        if op == "layernorm":
+            return lr.lr_layernorm_f32(xs[k], g, b, ys[k], rows, cols, eps, pol, sh, plan)
+        return lr.lr_cross_entropy_f32(xs[k], lab, ys[k], rows, cols, pol, sh, plan)
+    return run
+
+
+def _time(run, plan, iters, stream):
+    for i in range(5):
+        lr.check(run(i, plan), "warmup")
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(iters):
+        run(i, plan)
+    z.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(z) * 1e3 / iters
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description="exhaustive measured plan sweep for one shape")
+    ap.add_argument("--op", required=True, choices=sorted(lr.OPS))
+    ap.add_argument("--rows", type=int, required=True)
+    ap.add_argument("--cols", type=int, required=True)
+    ap.add_argument("--policy", default="unordered_tree", choices=sorted(lr.POLICIES))
+    ap.add_argument("--eps", type=float, default=1e-5)
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough for >= 1 GB)")
+    ap.add_argument("--iters", type=int, default=200)
+    ap.add_argument("--max-rows-per-block", type=int, default=4)
+    ap.add_argument("--json", action="store_true", help="one JSON line per candidate")
+    args = ap.parse_args(argv)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    rows, cols, op = args.rows, args.cols, args.op
+    tensor_bytes = rows * cols * 4
+    sets = args.sets or max(2, min(64, -(-(1 << 30) // (2 * tensor_bytes))))
+    gen = torch.Generator(device=dev).manual_seed(0)
+    x0 = torch.randn(rows, cols, device=dev, generator=gen)
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    if op == "cross_entropy":
+        ys = [torch.empty(rows, device=dev) for _ in range(sets)]
+    else:
+        ys = [torch.empty_like(x0) for _ in range(sets)]
+    g = torch.rand(cols, device=dev, generator=gen) + 0.5
+    b = torch.randn(cols, device=dev, generator=gen) * 0.1
+    lab = torch.randint(0, cols, (rows,), device=dev, generator=gen)
+    run = _launcher(op, xs, ys, g, b, lab, rows, cols, args.eps, args.policy, sh)
+
+    facts = lr.lr_device_facts_query()
+    aligned = 1 if cols % 4 == 0 else 0
+    auto = lr.lr_plan_query(op, rows, cols, args.policy)
+    lr.check(run(0, auto), "automatic plan")
+    torch.cuda.synchronize()
+    ref = ys[0].double().clone()
+    bound = 1e-6 + 1e-5 * ref.abs()
+
+    results = []
+    for p in lr.lr_plan_enumerate(facts, op, rows, cols, args.policy, aligned):
+        if p.rows_per_block > args.max_rows_per_block:
+            continue
+        st = run(0, p)
+        torch.cuda.synchronize()
+        valid = st == lr.LR_OK and bool(((ys[0].double() - ref).abs() <= bound).all())
+        us = _time(run, p, args.iters, stream) if valid else float("inf")
+        rec = dict(plan=p.as_dict(), us=us, valid=valid)
+        results.append((us, p, rec))
+        if args.json:
+            print(json.dumps(rec), flush=True)
+    results.sort(key=lambda t: t[0])
+    best_us, best, _ = results[0]
+    again = _time(run, best, args.iters, stream)
+    moved = 2 * tensor_bytes if op != "cross_entropy" else tensor_bytes + rows * 12
+    print(f"# {op} {rows}x{cols} {args.policy}: {len(results)} candidates, "
+          f"automatic {_time(run, auto, args.iters, stream):.2f} us, "
+          f"best {again:.2f} us ({moved / again / 1e3:.0f} GB/s): {best!r}")
+    for us, p, rec in results[:8]:
+        print(f"#   {us:8.2f} us  {p!r}")
+    fam = {0: "LR_FAMILY_CACHE", 1: "LR_FAMILY_STREAM", 2: "LR_FAMILY_ORDERED"}[best.family]
+    opn = {0: "LR_OP_SOFTMAX", 1: "LR_OP_RMSNORM", 2: "LR_OP_LAYERNORM", 3: "LR_OP_CROSS_ENTROPY"}[lr.OPS[op]]
+    pol = "LR_ORDERED_FOLD" if args.policy == "ordered_fold" else "LR_UNORDERED_TREE"
+    print(f"{{{opn}, {pol}, {rows}, {cols}, {aligned}, {fam}, {best.waves_per_row}, "
+          f"{best.rows_per_block}, {best.chunks_per_lane}}},")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

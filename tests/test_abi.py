@@ -1,0 +1,86 @@
+"""C-ABI boundary on the CPU: the library loads, exports every function that
+include/lr.h declares, and rejects bad arguments with the documented status
+before making any HIP call (no GPU is needed for any check here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_reductions_amd as lr
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lr.h")
+
+# Fake, well-aligned device addresses: validation never dereferences them.
+X = 0x7F0000000000
+Y = 0x7F0010000000
+G = 0x7F0020000000
+B = 0x7F0030000000
+LAB = 0x7F0040000000
+LOSS = 0x7F0050000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lr.lib, n), n
+    assert lr.lr_version().startswith("lr ")
+    for code, name in lr.STATUS.items():
+        assert lr.lr_status_string(code).startswith(name)
+
+
+def test_zero_rows_is_ok_without_launch():
+    # succeeds with no device present: nothing is launched and no HIP call is made
+    assert lr.lr_softmax_f32(X, Y, 0, 128, 0, 0) == lr.LR_OK
+    assert lr.lr_rmsnorm_f32(X, None, Y, 0, 5, 1e-6, 1, 0) == lr.LR_OK
+    assert lr.lr_layernorm_f32(X, None, None, Y, 0, 7, 1e-5, 0, 0) == lr.LR_OK
+    assert lr.lr_cross_entropy_f32(X, LAB, LOSS, 0, 32000, 0, 0) == lr.LR_OK
+
+
+@pytest.mark.parametrize("call,status", [
+    (lambda: lr.lr_softmax_f32(None, Y, 4, 8, 0, 0), lr.LR_ERR_NULL_POINTER),
+    (lambda: lr.lr_softmax_f32(X, None, 4, 8, 0, 0), lr.LR_ERR_NULL_POINTER),
+    (lambda: lr.lr_cross_entropy_f32(X, None, LOSS, 4, 8, 0, 0), lr.LR_ERR_NULL_POINTER),
+    (lambda: lr.lr_cross_entropy_f32(X, LAB, None, 4, 8, 0, 0), lr.LR_ERR_NULL_POINTER),
+    (lambda: lr.lr_softmax_f32(X, Y, -1, 8, 0, 0), lr.LR_ERR_INVALID_SHAPE),
+    (lambda: lr.lr_softmax_f32(X, Y, 4, 0, 0, 0), lr.LR_ERR_INVALID_SHAPE),
+    (lambda: lr.lr_softmax_f32(X, Y, 4, -3, 0, 0), lr.LR_ERR_INVALID_SHAPE),
+    (lambda: lr.lr_softmax_f32(X, Y, 4, 1 << 24, 0, 0), lr.LR_ERR_INVALID_SHAPE),
+    (lambda: lr.lr_softmax_f32(X, Y, 1 << 31, 8, 0, 0), lr.LR_ERR_INVALID_SHAPE),
+    (lambda: lr.lr_softmax_f32(X, Y, 4, 8, 2, 0), lr.LR_ERR_INVALID_POLICY),
+    (lambda: lr.lr_softmax_f32(X, Y, 4, 8, -1, 0), lr.LR_ERR_INVALID_POLICY),
+    (lambda: lr.lr_rmsnorm_f32(X, G, Y, 4, 8, float("nan"), 0, 0), lr.LR_ERR_INVALID_EPS),
+    (lambda: lr.lr_rmsnorm_f32(X, G, Y, 4, 8, float("inf"), 0, 0), lr.LR_ERR_INVALID_EPS),
+    (lambda: lr.lr_layernorm_f32(X, G, B, Y, 4, 8, -1e-5, 0, 0), lr.LR_ERR_INVALID_EPS),
+    (lambda: lr.lr_softmax_f32(X + 2, Y, 4, 8, 0, 0), lr.LR_ERR_MISALIGNED),
+    (lambda: lr.lr_rmsnorm_f32(X, G + 1, Y, 4, 8, 1e-6, 0, 0), lr.LR_ERR_MISALIGNED),
+    (lambda: lr.lr_cross_entropy_f32(X, LAB + 4, LOSS, 4, 8, 0, 0), lr.LR_ERR_MISALIGNED),
+    # partial overlap of input and output
+    (lambda: lr.lr_softmax_f32(X, X + 4, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_rmsnorm_f32(X, Y + 16, Y, 4, 8, 1e-6, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_layernorm_f32(X, G, Y + 8, Y, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_cross_entropy_f32(X, LAB, X + 64, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_cross_entropy_f32(X, LAB, LAB + 8, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
+])
+def test_validation_status_before_any_hip_call(call, status):
+    assert call() == status
+
+
+def test_with_plan_requires_plan():
+    f = ctypes.POINTER(lr.LrPlan)()
+    assert lr.lib.lr_softmax_f32_with_plan(X, Y, 4, 8, 0, f, 0) == lr.LR_ERR_NULL_POINTER
+
+
+def test_valid_call_without_device_reports_hip_error():
+    # arguments pass validation, then the device query fails on this CPU-only host
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is present")
+    assert lr.lr_softmax_f32(X, Y, 4, 8, 0, 0) == lr.LR_ERR_HIP
+    assert lr.lr_softmax_f32(X, X, 4, 8, 0, 0) == lr.LR_ERR_HIP  # in place is allowed

@@ -1,0 +1,131 @@
+"""Planner on the CPU: every legal plan covers each (row, element) exactly
+once (the coverage requirement of "TIRx Metal reduction lowering", section
+4.4, checked by replaying the kernels' own index functions), plans respect
+the device limits, explicit plans are honoured or rejected but never
+clamped, and the automatic choice is deterministic."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import row_reductions_amd as lr
+
+F = lr.lr_device_facts_mi355x()
+OPS = ["softmax", "rmsnorm", "layernorm", "cross_entropy"]
+
+WIDTHS = list(range(1, 131)) + [255, 256, 257, 511, 513, 1023, 1024, 1025, 1537, 3072, 6144, 12289]
+
+
+def coverage(plan, rows, cols, phase):
+    counts = np.zeros(rows * cols, dtype=np.uint32)
+    st = lr.lr_coverage_check(plan, rows, cols, phase, counts.ctypes.data)
+    assert st == lr.LR_OK
+    return counts
+
+
+@pytest.mark.parametrize("policy", ["unordered_tree", "ordered_fold"])
+def test_every_plan_covers_each_element_once(policy):
+    checked = 0
+    for cols in WIDTHS:
+        rows = 5 if cols < 2000 else 2
+        aligned_opts = (1, 0) if cols % 4 == 0 else (0,)
+        for aligned in aligned_opts:
+            plans = lr.lr_plan_enumerate(F, "softmax", rows, cols, policy, aligned)
+            assert plans, (cols, aligned)
+            phases = (0,) if aligned else (0, 1, 2, 3)
+            for p in plans:
+                for ph in phases:
+                    c = coverage(p, rows, cols, ph)
+                    assert (c == 1).all(), (cols, aligned, ph, p)
+                    checked += 1
+    assert checked > 1000
+
+
+def test_config_shapes_every_plan_covers_once():
+    for rows, cols in [(37, 1537), (256, 3072), (64, 12289), (3, 6144), (2, 32000)]:
+        aligned = 1 if cols % 4 == 0 else 0
+        for p in lr.lr_plan_enumerate(F, "cross_entropy", rows, cols, "unordered_tree", aligned):
+            for ph in ((0,) if aligned else (0, 3)):
+                assert (coverage(p, rows, cols, ph) == 1).all(), (rows, cols, p)
+
+
+def test_plans_respect_device_limits():
+    for op in OPS:
+        for rows, cols in [(1, 1), (37, 1537), (768, 6144), (4096, 32000), (5, 100000)]:
+            for policy in ("unordered_tree", "ordered_fold"):
+                for p in lr.lr_plan_enumerate(F, op, rows, cols, policy, 1 if cols % 4 == 0 else 0):
+                    assert p.threads_per_block == 64 * p.waves_per_row * p.rows_per_block <= 1024
+                    assert p.blocks == -(-rows // p.rows_per_block)
+                    assert p.lds_bytes <= 64 * 1024
+                    if p.family == lr.LR_FAMILY_CACHE:
+                        need = -(-((cols + 6) // 4 if cols % 4 else cols // 4) // (64 * p.waves_per_row))
+                        assert p.chunks_per_lane >= need
+                        assert p.chunks_per_lane in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32)
+                    if policy == "ordered_fold":
+                        assert p.family == lr.LR_FAMILY_ORDERED and p.waves_per_row == 1
+
+
+def test_automatic_plan_is_legal_and_deterministic():
+    for op in OPS:
+        for rows, cols in [(37, 1537), (256, 3072), (64, 12289), (768, 6144), (4096, 32000), (7, 4096),
+                           (1, 1), (100000, 64)]:
+            for policy in ("unordered_tree", "ordered_fold"):
+                al = 1 if cols % 4 == 0 else 0
+                a = lr.lr_plan_for_device(F, op, rows, cols, policy, al)
+                b = lr.lr_plan_for_device(F, op, rows, cols, policy, al)
+                assert bytes(a) == bytes(b)
+                assert lr.lr_plan_validate(F, op, rows, cols, policy, al, a) == lr.LR_OK
+
+
+def _plan(**kw):
+    p = lr.lr_plan_for_device(F, "softmax", 768, 6144, "unordered_tree", 1)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("change", [
+    dict(chunks_per_lane=5),                                 # no compiled instance
+    dict(waves_per_row=1, threads_per_block=64, chunks_per_lane=6),  # stripe too small for the row
+    dict(threads_per_block=512),                             # inconsistent with 64*S*Q
+    dict(rows_per_block=3, threads_per_block=64 * 4 * 3, blocks=256),  # fine shape, wrong... S*Q ok
+    dict(waves_per_row=17, threads_per_block=64 * 17),       # S out of range
+    dict(blocks=1),                                          # wrong block count
+    dict(family=lr.LR_FAMILY_ORDERED),                       # family does not match policy
+    dict(vec=2),
+])
+def test_unrealizable_explicit_plan_is_rejected_not_clamped(change):
+    p = _plan(**change)
+    st = lr.lr_plan_validate(F, "softmax", 768, 6144, "unordered_tree", 1, p)
+    if change.get("rows_per_block") == 3:
+        # S=4, Q=3 is a legal shape: honoured exactly
+        assert st == lr.LR_OK
+    else:
+        assert st == lr.LR_ERR_UNREALIZABLE_PLAN
+
+
+def test_ordered_policy_rejects_unordered_plan():
+    p = lr.lr_plan_for_device(F, "rmsnorm", 256, 3072, "unordered_tree", 1)
+    assert lr.lr_plan_validate(F, "rmsnorm", 256, 3072, "ordered_fold", 1, p) == lr.LR_ERR_UNREALIZABLE_PLAN
+    q = lr.lr_plan_for_device(F, "rmsnorm", 256, 3072, "ordered_fold", 1)
+    assert q.family == lr.LR_FAMILY_ORDERED
+    assert lr.lr_plan_validate(F, "rmsnorm", 256, 3072, "unordered_tree", 1, q) == lr.LR_ERR_UNREALIZABLE_PLAN
+
+
+def test_cache_plan_for_aligned_rows_does_not_cover_misaligned_rows():
+    # 6144 floats over S=4 waves is exactly 6 chunks per lane when rows are
+    # 16-byte aligned; a misaligned row touches one more chunk
+    p = _plan(family=lr.LR_FAMILY_CACHE, waves_per_row=4, rows_per_block=1, threads_per_block=256,
+              blocks=768, chunks_per_lane=6)
+    assert lr.lr_plan_validate(F, "softmax", 768, 6144, "unordered_tree", 1, p) == lr.LR_OK
+    assert lr.lr_plan_validate(F, "softmax", 768, 6144, "unordered_tree", 0, p) == lr.LR_ERR_UNREALIZABLE_PLAN
+
+
+def test_planner_argument_errors():
+    p = lr.LrPlan()
+    assert lr.lib.lr_plan_for_device(ctypes.byref(F), 7, 4, 4, 0, 1, ctypes.byref(p)) == lr.LR_ERR_INVALID_ARGUMENT
+    assert lr.lib.lr_plan_for_device(ctypes.byref(F), 0, 4, 4, 5, 1, ctypes.byref(p)) == lr.LR_ERR_INVALID_POLICY
+    assert lr.lib.lr_plan_for_device(ctypes.byref(F), 0, 4, 0, 0, 1, ctypes.byref(p)) == lr.LR_ERR_INVALID_SHAPE
+    n = ctypes.c_int32(-1)
+    assert lr.lib.lr_plan_enumerate(ctypes.byref(F), 0, 4, 4, 0, 1, None, 0, ctypes.byref(n)) == lr.LR_OK
+    assert n.value > 0
