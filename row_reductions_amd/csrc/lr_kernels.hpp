@@ -59,25 +59,37 @@ __device__ __forceinline__ float4 param_chunk(const float* p, int k, int h, int 
     return g;
 }
 
-// Aligned rows: chunk k of a parameter vector loaded without a branch.  An
-// absent parameter reads the row instead (a valid address) and returns
-// `fill`, so the load phase is straight-line code.
-__device__ __forceinline__ float4 param_chunk_aligned(const float* p, const float* any_valid, int k,
-                                                      float fill) {
-    const float4 raw = ld4_cached(reinterpret_cast<const float4*>(p ? p : any_valid) + k);
-    return p ? raw : splat4(fill);
+// How a kernel instance reads the per-column parameters (gamma, beta).
+//   kParNone:    no parameter present; nothing is loaded.
+//   kParAll:     every parameter the op uses is present; loads need no test.
+//   kParRuntime: some present, some not; each load tests its pointer.
+// Keeping presence a compile-time property leaves the load phase
+// straight-line code, so each wait covers only the loads it needs.
+enum ParamMode : int { kParNone = 0, kParAll = 1, kParRuntime = 2 };
+
+template <bool AL, int PM>
+__device__ __forceinline__ float4 load_param(const float* p, int k, int h, int cols, float fill) {
+    if constexpr (PM == kParNone) {
+        return splat4(fill);
+    } else if constexpr (PM == kParAll && AL) {
+        return ld4_cached(reinterpret_cast<const float4*>(p) + k);
+    } else {
+        return param_chunk<AL>(p, k, h, cols, fill);
+    }
 }
 
 // ===========================================================================
 // CACHE family: worker w keeps chunks k = w + W*c, c < NCH, in registers.
+// The per-column parameters are read in the store loop, after the
+// reductions: issued next to the row loads they compete with them for the
+// CU's texture path while the row is still arriving, which measured slower
+// on MI355X (as did staging them in LDS once per workgroup).
 // ===========================================================================
-template <int OP, int NCH, bool AL>
+template <int OP, int NCH, bool AL, int PM>
 __global__ void __launch_bounds__(cache_max_threads(NCH))
 k_cache(const KArgs a) {
     __shared__ float red[2][kMaxWaves];
     constexpr float ID = op_identity<OP>();
-    // parameter chunks held in registers early (bounded so the stripe does not spill)
-    constexpr bool kPrefetch = (OP == kLayerNorm) ? NCH <= 6 : NCH <= 8;
     const int S = a.S;
     const int W = kWave * S;
     const Team t = team_of((int)threadIdx.x, S);
@@ -139,16 +151,6 @@ k_cache(const KArgs a) {
             }
         }
     } else if constexpr (OP == kRmsNorm) {
-        // short stripes: fetch gamma now so its latency hides behind the reduction
-        float4 gp[kPrefetch ? NCH : 1];
-        if constexpr (kPrefetch) {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int k = chunk_index(t.w, W, c);
-                gp[c] = AL ? param_chunk_aligned(a.gamma, xr, min(k, klast), 1.0f)
-                           : param_chunk<AL>(a.gamma, min(k, klast), h, cols, 1.0f);
-            }
-        }
         float ss = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
@@ -160,24 +162,13 @@ k_cache(const KArgs a) {
         for (int c = 0; c < NCH; ++c) {
             const int k = chunk_index(t.w, W, c);
             if (k < nv) {
-                const float4 g = kPrefetch ? gp[c] : param_chunk<AL>(a.gamma, k, h, cols, 1.0f);
+                const float4 g = load_param<AL, PM>(a.gamma, k, h, cols, 1.0f);
                 const float4 o = make_float4(v[c].x * r * g.x, v[c].y * r * g.y,
                                              v[c].z * r * g.z, v[c].w * r * g.w);
                 store_chunk<AL>(a, yr, k, h, o);
             }
         }
     } else {  // kLayerNorm
-        float4 gp[kPrefetch ? NCH : 1], bp[kPrefetch ? NCH : 1];
-        if constexpr (kPrefetch) {
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int k = chunk_index(t.w, W, c);
-                gp[c] = AL ? param_chunk_aligned(a.gamma, xr, min(k, klast), 1.0f)
-                           : param_chunk<AL>(a.gamma, min(k, klast), h, cols, 1.0f);
-                bp[c] = AL ? param_chunk_aligned(a.beta, xr, min(k, klast), 0.0f)
-                           : param_chunk<AL>(a.beta, min(k, klast), h, cols, 0.0f);
-            }
-        }
         float sum = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) sum += (v[c].x + v[c].y) + (v[c].z + v[c].w);
@@ -200,8 +191,8 @@ k_cache(const KArgs a) {
         for (int c = 0; c < NCH; ++c) {
             const int k = chunk_index(t.w, W, c);
             if (k < nv) {
-                const float4 g = kPrefetch ? gp[c] : param_chunk<AL>(a.gamma, k, h, cols, 1.0f);
-                const float4 b = kPrefetch ? bp[c] : param_chunk<AL>(a.beta, k, h, cols, 0.0f);
+                const float4 g = load_param<AL, PM>(a.gamma, k, h, cols, 1.0f);
+                const float4 b = load_param<AL, PM>(a.beta, k, h, cols, 0.0f);
                 const float4 o = make_float4(v[c].x * r * g.x + b.x, v[c].y * r * g.y + b.y,
                                              v[c].z * r * g.z + b.z, v[c].w * r * g.w + b.w);
                 store_chunk<AL>(a, yr, k, h, o);
@@ -357,33 +348,47 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
 // ---------------------------------------------------------------------------
 // Launch by plan: selects the compiled instance and launches it on `s`.
 // ---------------------------------------------------------------------------
-template <int OP, int NCH, bool AL>
+template <int OP, int NCH, bool AL, int PM>
 hipError_t launch_cache_inst(const KArgs& a, const lr_plan& p, hipStream_t s) {
-    hipLaunchKernelGGL((k_cache<OP, NCH, AL>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+    hipLaunchKernelGGL((k_cache<OP, NCH, AL, PM>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
     return hipGetLastError();
 }
 
-template <int OP, bool AL>
-hipError_t launch_cache_al(const KArgs& a, const lr_plan& p, hipStream_t s) {
+template <int OP, bool AL, int PM>
+hipError_t launch_cache_nch(const KArgs& a, const lr_plan& p, hipStream_t s) {
     switch (p.chunks_per_lane) {
-        case 1: return launch_cache_inst<OP, 1, AL>(a, p, s);
-        case 2: return launch_cache_inst<OP, 2, AL>(a, p, s);
-        case 3: return launch_cache_inst<OP, 3, AL>(a, p, s);
-        case 4: return launch_cache_inst<OP, 4, AL>(a, p, s);
-        case 6: return launch_cache_inst<OP, 6, AL>(a, p, s);
-        case 8: return launch_cache_inst<OP, 8, AL>(a, p, s);
-        case 12: return launch_cache_inst<OP, 12, AL>(a, p, s);
-        case 16: return launch_cache_inst<OP, 16, AL>(a, p, s);
-        case 24: return launch_cache_inst<OP, 24, AL>(a, p, s);
-        case 32: return launch_cache_inst<OP, 32, AL>(a, p, s);
+        case 1: return launch_cache_inst<OP, 1, AL, PM>(a, p, s);
+        case 2: return launch_cache_inst<OP, 2, AL, PM>(a, p, s);
+        case 3: return launch_cache_inst<OP, 3, AL, PM>(a, p, s);
+        case 4: return launch_cache_inst<OP, 4, AL, PM>(a, p, s);
+        case 6: return launch_cache_inst<OP, 6, AL, PM>(a, p, s);
+        case 8: return launch_cache_inst<OP, 8, AL, PM>(a, p, s);
+        case 12: return launch_cache_inst<OP, 12, AL, PM>(a, p, s);
+        case 16: return launch_cache_inst<OP, 16, AL, PM>(a, p, s);
+        case 24: return launch_cache_inst<OP, 24, AL, PM>(a, p, s);
+        case 32: return launch_cache_inst<OP, 32, AL, PM>(a, p, s);
         default: return hipErrorInvalidValue;
+    }
+}
+
+// Selects the parameter mode from which parameters are present.
+template <int OP, bool AL>
+hipError_t launch_cache_pm(const KArgs& a, const lr_plan& p, hipStream_t s) {
+    if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
+        return launch_cache_nch<OP, AL, kParNone>(a, p, s);
+    } else {
+        const bool all = a.gamma != nullptr && (OP == kRmsNorm || a.beta != nullptr);
+        const bool none = a.gamma == nullptr && (OP == kRmsNorm || a.beta == nullptr);
+        if (all) return launch_cache_nch<OP, AL, kParAll>(a, p, s);
+        if (none) return launch_cache_nch<OP, AL, kParNone>(a, p, s);
+        return launch_cache_nch<OP, AL, kParRuntime>(a, p, s);
     }
 }
 
 template <int OP>
 hipError_t launch_op(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s) {
     if (p.family == LR_FAMILY_CACHE) {
-        return aligned ? launch_cache_al<OP, true>(a, p, s) : launch_cache_al<OP, false>(a, p, s);
+        return aligned ? launch_cache_pm<OP, true>(a, p, s) : launch_cache_pm<OP, false>(a, p, s);
     }
     if (p.family == LR_FAMILY_STREAM) {
         if (aligned)
