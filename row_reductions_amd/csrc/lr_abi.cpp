@@ -133,6 +133,7 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     a.inv_cols = 1.0f / (float)c.cols;
     a.S = plan.waves_per_row;
     a.Q = plan.rows_per_block;
+    a.team_magic = team_magic(plan.waves_per_row);
     a.y_same_phase = ce ? 1
                         : (int32_t)((reinterpret_cast<uintptr_t>(c.y) & 15u) ==
                                     (reinterpret_cast<uintptr_t>(c.x) & 15u));

@@ -33,8 +33,13 @@ struct AddOp {
     static __device__ __forceinline__ float apply(float a, float b) { return a + b; }
     static constexpr float identity() { return 0.0f; }
 };
+// Max of two floats: IEEE 754-2019 maximum (v_maximum*_f32 on gfx950; NaN
+// propagates), which needs no input canonicalisation and folds three
+// operands per instruction.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 struct MaxOp {
-    static __device__ __forceinline__ float apply(float a, float b) { return fmaxf(a, b); }
+    static __device__ __forceinline__ float apply(float a, float b) { return fmax2(a, b); }
     static constexpr float identity() { return -INFINITY; }
 };
 
@@ -115,6 +120,47 @@ __device__ __forceinline__ void st4(float4* p, float4 v) {
     } else {
         *p = v;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources.  A resource covers `bytes` bytes from a wave-uniform base;
+// a load past the end returns 0 and a store past the end is dropped, so
+// straight-line code needs no per-lane bounds test to stay inside the range.
+// Offsets passed here are never negative.  A null base with 0 bytes is a valid
+// empty resource (every load returns 0).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+constexpr int kAuxNt = 2;  // cache policy: nontemporal (streamed once)
+constexpr int kAuxDefault = 0;
+
+__device__ __forceinline__ uint64_t wave_uniform(uint64_t u) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Word 3 of the resource: 32-bit data format, raw (unswizzled) addressing.
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ BufRes make_res(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(wave_uniform(reinterpret_cast<uint64_t>(base))),
+                                             (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
+}
+
+template <int AUX>
+__device__ __forceinline__ float4 res_ld4(BufRes r, int byte_off) {
+    const v4f v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, AUX);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float res_ld1(BufRes r, int byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kAuxDefault));
+}
+
+__device__ __forceinline__ void res_st4(BufRes r, int byte_off, float4 v) {
+    const v4f w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, byte_off, 0, LR_NT_STORES ? kAuxNt : kAuxDefault);
 }
 
 __device__ __forceinline__ float get(const float4& v, int j) {

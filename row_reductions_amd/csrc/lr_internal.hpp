@@ -24,6 +24,7 @@ struct KArgs {
     int32_t S;              // waves per row
     int32_t Q;              // rows per workgroup
     int32_t y_same_phase;   // y rows start at the same 16-byte phase as x rows
+    int32_t team_magic;     // team_magic(S): wave index / S as a multiply
 };
 
 // Compiled cache-family chunk counts (chunks_per_lane), ascending.

@@ -46,6 +46,7 @@ __device__ __forceinline__ void store_chunk(const KArgs& a, float* yr, int k, in
 }
 
 // Per-column parameter (gamma or beta) for chunk k; `fill` where absent.
+// Used by the STREAM family.
 template <bool AL>
 __device__ __forceinline__ float4 param_chunk(const float* p, int k, int h, int cols, float fill) {
     if (p == nullptr) return splat4(fill);
@@ -61,58 +62,94 @@ __device__ __forceinline__ float4 param_chunk(const float* p, int k, int h, int 
 
 // How a kernel instance reads the per-column parameters (gamma, beta).
 //   kParNone:    no parameter present; nothing is loaded.
-//   kParAll:     every parameter the op uses is present; loads need no test.
-//   kParRuntime: some present, some not; each load tests its pointer.
-// Keeping presence a compile-time property leaves the load phase
-// straight-line code, so each wait covers only the loads it needs.
+//   kParAll:     every parameter the op uses is present.
+//   kParRuntime: some present, some not; absent ones read an empty resource
+//                (zeros) and take their fill value.
 enum ParamMode : int { kParNone = 0, kParAll = 1, kParRuntime = 2 };
 
+// Chunk k of a parameter vector read through its resource `r` (cols floats,
+// or empty when the parameter is absent), in the row's 16-byte grid of phase
+// h.  Straight-line: a chunk past the end reads zeros (aligned rows); on
+// misaligned rows each float is read at a clamped in-range index and grid
+// slots outside the row are never used.
 template <bool AL, int PM>
-__device__ __forceinline__ float4 load_param(const float* p, int k, int h, int cols, float fill) {
+__device__ __forceinline__ float4 param_load(BufRes r, bool present, int k, int h, int cols, float fill) {
     if constexpr (PM == kParNone) {
         return splat4(fill);
-    } else if constexpr (PM == kParAll && AL) {
-        return ld4_cached(reinterpret_cast<const float4*>(p) + k);
     } else {
-        return param_chunk<AL>(p, k, h, cols, fill);
+        float4 g;
+        if constexpr (AL) {
+            g = res_ld4<kAuxDefault>(r, k * 16);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const int e = min(max(elem_index(k, j, h), 0), cols - 1);
+                set(g, j, res_ld1(r, e * 4));
+            }
+        }
+        if constexpr (PM == kParRuntime) {
+            if (!present) g = splat4(fill);
+        }
+        return g;
     }
 }
 
+// Parameters of a norm (gamma; gamma and beta for LayerNorm).
+template <int OP>
+constexpr int num_params() {
+    return OP == kLayerNorm ? 2 : (OP == kRmsNorm ? 1 : 0);
+}
+
+// Wave index within the workgroup, as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 // ===========================================================================
 // CACHE family: worker w keeps chunks k = w + W*c, c < NCH, in registers.
-// The per-column parameters are read in the store loop, after the
-// reductions: issued next to the row loads they compete with them for the
-// CU's texture path while the row is still arriving, which measured slower
-// on MI355X (as did staging them in LDS once per workgroup).
+//
+// Row, team and base addresses are wave-uniform and live in scalar
+// registers.  The row is read through a buffer resource covering its chunks,
+// so every load is issued unconditionally (a slot past the row's last chunk
+// reads zeros and then takes the identity) and each wait covers only the
+// loads it needs.
+//
+// The per-column parameters are read chunk by chunk in the store loop.  Every
+// workgroup reads the same few kilobytes of gamma/beta, so the alternatives
+// measured on MI355X (768 x 6144) concentrate requests on the same L2 lines:
+// issuing them with the row loads, or as one burst per wave before the last
+// reduction, was 0.3-2 us slower; rotating each workgroup's chunk order to
+// spread those requests cost more in the row stream than it saved.
 // ===========================================================================
 template <int OP, int NCH, bool AL, int PM>
 __global__ void __launch_bounds__(cache_max_threads(NCH))
 k_cache(const KArgs a) {
     __shared__ float red[2][kMaxWaves];
     constexpr float ID = op_identity<OP>();
+    constexpr int NP = num_params<OP>();
     const int S = a.S;
     const int W = kWave * S;
-    const Team t = team_of((int)threadIdx.x, S);
+    const Team t = team_of_wave(wave_id(), (int)threadIdx.x & (kWave - 1), S, a.team_magic);
     const int64_t row = row_of(blockIdx.x, a.Q, t.q);
     const bool active = row < a.rows;
     const int cols = a.cols;
     const float* xr = a.x + (active ? row : 0) * (int64_t)cols;
     const int h = AL ? 0 : phase_of(reinterpret_cast<uintptr_t>(xr));
     const int nv = active ? (AL ? cols / kVec : chunks_of(h, cols)) : 0;
-    const float4* xa = reinterpret_cast<const float4*>(xr - h);
+    const BufRes rx = make_res(xr - h, nv * 16);
+    const BufRes rg = make_res(a.gamma, NP >= 1 && a.gamma ? cols * 4 : 0);
+    const BufRes rb = make_res(a.beta, NP == 2 && a.beta ? cols * 4 : 0);
+    auto chunk = [&](int c) { return chunk_index(t.w, W, c); };
 
-    // Every load is issued unconditionally (straight-line code, so each wait
-    // covers only the loads it needs): a slot past the row's last chunk
-    // re-reads that last chunk -- always a valid address; an inactive team
-    // reads the tensor's first chunk -- and then takes the identity instead.
-    const int klast = (nv > 0 ? nv : 1) - 1;
     float4 v[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int k = chunk_index(t.w, W, c);
-        const float4 raw = ld4(xa + min(k, klast));
-        v[c] = (k < nv) ? raw : splat4(ID);
-        if (!AL) mask_chunk(v[c], k, h, cols, ID);
+        const int k = chunk(c);
+        const float4 raw = res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rx, k * 16);
+        if constexpr (ID == 0.0f && AL) {
+            v[c] = raw;  // past the end: zeros, the add identity
+        } else {
+            v[c] = (k < nv) ? raw : splat4(ID);
+            if (!AL) mask_chunk(v[c], k, h, cols, ID);
+        }
     }
 
     float sel = 0.0f;
@@ -123,8 +160,7 @@ k_cache(const KArgs a) {
     if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
         float m = ID;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
-            m = fmaxf(fmaxf(m, fmaxf(v[c].x, v[c].y)), fmaxf(v[c].z, v[c].w));
+        for (int c = 0; c < NCH; ++c) m = fmax2(fmax2(m, fmax2(v[c].x, v[c].y)), fmax2(v[c].z, v[c].w));
         m = team_reduce<MaxOp>(m, red[0], S, t);
         float s = 0.0f;
 #pragma unroll
@@ -143,7 +179,7 @@ k_cache(const KArgs a) {
             float* yr = a.y + row * (int64_t)cols;
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                const int k = chunk_index(t.w, W, c);
+                const int k = chunk(c);
                 if (k < nv) {
                     const float4 o = make_float4(v[c].x * r, v[c].y * r, v[c].z * r, v[c].w * r);
                     store_chunk<AL>(a, yr, k, h, o);
@@ -160,9 +196,9 @@ k_cache(const KArgs a) {
         float* yr = a.y + row * (int64_t)cols;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int k = chunk_index(t.w, W, c);
+            const int k = chunk(c);
             if (k < nv) {
-                const float4 g = load_param<AL, PM>(a.gamma, k, h, cols, 1.0f);
+                const float4 g = param_load<AL, PM>(rg, a.gamma != nullptr, k, h, cols, 1.0f);
                 const float4 o = make_float4(v[c].x * r * g.x, v[c].y * r * g.y,
                                              v[c].z * r * g.z, v[c].w * r * g.w);
                 store_chunk<AL>(a, yr, k, h, o);
@@ -177,7 +213,7 @@ k_cache(const KArgs a) {
         float qs = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int k = chunk_index(t.w, W, c);
+            const int k = chunk(c);
             float4 d = make_float4(v[c].x - mu, v[c].y - mu, v[c].z - mu, v[c].w - mu);
             if (k >= nv) d = splat4(0.0f);
             if (!AL) mask_chunk(d, k, h, cols, 0.0f);
@@ -189,10 +225,10 @@ k_cache(const KArgs a) {
         float* yr = a.y + row * (int64_t)cols;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int k = chunk_index(t.w, W, c);
+            const int k = chunk(c);
             if (k < nv) {
-                const float4 g = load_param<AL, PM>(a.gamma, k, h, cols, 1.0f);
-                const float4 b = load_param<AL, PM>(a.beta, k, h, cols, 0.0f);
+                const float4 g = param_load<AL, PM>(rg, a.gamma != nullptr, k, h, cols, 1.0f);
+                const float4 b = param_load<AL, PM>(rb, a.beta != nullptr, k, h, cols, 0.0f);
                 const float4 o = make_float4(v[c].x * r * g.x + b.x, v[c].y * r * g.y + b.y,
                                              v[c].z * r * g.z + b.z, v[c].w * r * g.w + b.w);
                 store_chunk<AL>(a, yr, k, h, o);
@@ -224,7 +260,7 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
     constexpr float ID = op_identity<OP>();
     const int S = a.S;
     const int W = kWave * S;
-    const Team t = team_of((int)threadIdx.x, S);
+    const Team t = team_of_wave(wave_id(), (int)threadIdx.x & (kWave - 1), S, a.team_magic);
     const int64_t row = row_of(blockIdx.x, a.Q, t.q);
     const bool active = row < a.rows;
     const int cols = a.cols;
@@ -247,7 +283,7 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
             float tm = m;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                tm = fmaxf(fmaxf(tm, fmaxf(v[u].x, v[u].y)), fmaxf(v[u].z, v[u].w));
+                tm = fmax2(fmax2(tm, fmax2(v[u].x, v[u].y)), fmax2(v[u].z, v[u].w));
             s *= fast_exp(m - tm);  // m = -inf on the first trip: s is 0 anyway
             m = tm;
 #pragma unroll

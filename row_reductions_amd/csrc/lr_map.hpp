@@ -34,12 +34,21 @@ struct Team {
     int lane;  // lane within the wavefront
 };
 
-LR_HD Team team_of(int tid, int S) {
-    const int W = kWave * S;
-    const int q = tid / W;
-    const int w = tid - q * W;
-    return Team{q, w, w / kWave, tid % kWave};
+// Multiplier that turns the division of a wave index by S into a multiply
+// and a shift: floor(i / S) == (i * team_magic(S)) >> 16 for 0 <= i < 16 and
+// 1 <= S <= 16 (ceil(2^16/S) exceeds 2^16/S by less than 1, and i times that
+// excess stays below 2^16/S, so the quotient never reaches the next integer).
+LR_HD int team_magic(int S) { return (65536 + S - 1) / S; }
+
+// Team of lane `lane` of wave `wave` of a workgroup whose row teams are S
+// waves wide.  Every field but `w` and `lane` is uniform over the wave.
+LR_HD Team team_of_wave(int wave, int lane, int S, int magic) {
+    const int q = (wave * magic) >> 16;
+    const int s = wave - q * S;
+    return Team{q, s * kWave + lane, s, lane};
 }
+
+LR_HD Team team_of(int tid, int S) { return team_of_wave(tid / kWave, tid % kWave, S, team_magic(S)); }
 
 LR_HD int64_t row_of(int64_t block, int Q, int q) { return block * Q + q; }
 
