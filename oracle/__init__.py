@@ -49,6 +49,8 @@ def _load():
         lib.oracle_layernorm_f64.argtypes = [P, P, P, P, I64, I64, ctypes.c_double]
         lib.oracle_layernorm_stats_f64.argtypes = [P, P, P, I64, I64]
         lib.oracle_cross_entropy_f64.argtypes = [P, P, P, I64, I64]
+        lib.oracle_add_layernorm_f64.argtypes = [P, P, P, P, P, P, I64, I64, ctypes.c_double]
+        lib.oracle_add_layernorm_f64.restype = ctypes.c_int
         lib.oracle_rmsnorm_fold_f32.argtypes = [P, P, P, I64, I64, ctypes.c_float]
         lib.oracle_layernorm_fold_f32.argtypes = [P, P, P, P, I64, I64, ctypes.c_float]
         lib.oracle_fold_left_f32.argtypes = [P, I64, ctypes.c_int]
@@ -111,6 +113,23 @@ def layernorm(x, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
     return y
 
 
+def add_layernorm(x, residual, gamma=None, beta=None, eps: float = 1e-5, with_sum: bool = False):
+    """Fused residual LayerNorm: layernorm(fl32(x + residual)) in double; with
+    ``with_sum`` also the FP32 combined tensor."""
+    x = _f32(x)
+    r = _f32(residual)
+    assert r.shape == x.shape
+    g = _opt_vec(gamma, x.shape[1])
+    b = _opt_vec(beta, x.shape[1])
+    y = np.empty(x.shape, dtype=np.float64)
+    s = np.empty(x.shape, dtype=np.float32) if with_sum else None
+    rc = _load().oracle_add_layernorm_f64(_ptr(x), _ptr(r), _ptr(g), _ptr(b), _ptr(y), _ptr(s),
+                                          x.shape[0], x.shape[1], eps_as_f32(eps))
+    if rc != 0:
+        raise MemoryError("oracle_add_layernorm_f64: row scratch")
+    return (y, s) if with_sum else y
+
+
 def layernorm_stats(x):
     x = _f32(x)
     mu = np.empty(x.shape[0], dtype=np.float64)
@@ -163,4 +182,6 @@ def run(op: str, inputs: dict, eps=None) -> np.ndarray:
         return layernorm(inputs["x"], inputs.get("gamma"), inputs.get("beta"), eps)
     if op == "cross_entropy":
         return cross_entropy(inputs["logits"], inputs["labels"])
+    if op == "add_layernorm":
+        return add_layernorm(inputs["x"], inputs["residual"], inputs.get("gamma"), inputs.get("beta"), eps)
     raise ValueError(op)

@@ -8,6 +8,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 /* Row softmax: the source program of section 1 of "TIRx Metal reduction
  * lowering" takes exp of the row minus its maximum, then divides by the sum
@@ -84,6 +85,35 @@ void oracle_layernorm_f64(const float* x, const float* gamma, const float* beta,
             yr[j] = ((double)xr[j] - mu) / d * g + b;
         }
     }
+}
+
+/* Fused residual LayerNorm: section 5.1 of "TIRx Metal reduction lowering"
+ * forms combined = X + residual elementwise in the tile's FP32 arithmetic and
+ * takes the two-pass LayerNorm of combined (mean, centred values, variance,
+ * centred / sqrt(variance + eps)).  The affine step and the optional copy of
+ * combined are this library's additions; with gamma = beta = NULL the result
+ * is the pages' program.  The FP32 sum is formed here with one float
+ * addition per element (C float arithmetic, no contraction), the rest in
+ * double as oracle_layernorm_f64. */
+int oracle_add_layernorm_f64(const float* x, const float* res, const float* gamma,
+                             const float* beta, double* y, float* sum_out,
+                             int64_t rows, int64_t cols, double eps) {
+    float* c = (float*)malloc((size_t)cols * sizeof(float));
+    if (c == NULL) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        const float* rr = res + r * cols;
+        for (int64_t j = 0; j < cols; ++j) {
+            const float sum = xr[j] + rr[j];
+            c[j] = sum;
+        }
+        oracle_layernorm_f64(c, gamma, beta, y + r * cols, 1, cols, eps);
+        if (sum_out != NULL) {
+            for (int64_t j = 0; j < cols; ++j) sum_out[r * cols + j] = c[j];
+        }
+    }
+    free(c);
+    return 0;
 }
 
 /* Cross-entropy: section 1 composes peak = max(row), total = sum exp(row -

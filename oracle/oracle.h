@@ -45,6 +45,14 @@ void oracle_rmsnorm_f64(const float* x, const float* gamma, double* y,
 void oracle_layernorm_f64(const float* x, const float* gamma, const float* beta,
                           double* y, int64_t rows, int64_t cols, double eps);
 
+/* Fused residual LayerNorm: combined = fl32(x + res) elementwise (one FP32
+ * addition), then y = layernorm(combined) as above (double).  sum_out, when
+ * not NULL, receives combined (rows*cols floats).  Returns 0, or -1 when the
+ * row scratch cannot be allocated. */
+int oracle_add_layernorm_f64(const float* x, const float* res, const float* gamma,
+                             const float* beta, double* y, float* sum_out,
+                             int64_t rows, int64_t cols, double eps);
+
 /* Row statistics of LayerNorm (mean and biased variance), for invariant tests. */
 void oracle_layernorm_stats_f64(const float* x, double* mean, double* var,
                                 int64_t rows, int64_t cols);

@@ -36,6 +36,7 @@ STREAM_X = 0
 STREAM_GAMMA = 1
 STREAM_BETA = 2
 STREAM_LABELS = 3
+STREAM_RESIDUAL = 4
 
 _CHUNK = 1 << 22  # values generated per numpy pass (bounds temporary memory)
 
@@ -137,6 +138,15 @@ def layernorm_inputs(rows: int, cols: int, seed: int = 0, mean: float = 0.0,
     }
 
 
+def add_layernorm_inputs(rows: int, cols: int, seed: int = 0, mean: float = 0.0,
+                         std: float = 1.0) -> dict:
+    """Fused residual LayerNorm: x and residual N(mean, std^2) from their own
+    streams, gamma and beta as for LayerNorm."""
+    d = layernorm_inputs(rows, cols, seed, mean, std)
+    d["residual"] = normal_f32(seed, STREAM_RESIDUAL, rows * cols, mean, std).reshape(rows, cols)
+    return d
+
+
 def cross_entropy_inputs(rows: int, cols: int, seed: int = 0, std: float = 2.0) -> dict:
     return {
         "logits": normal_f32(seed, STREAM_X, rows * cols, 0.0, std).reshape(rows, cols),
@@ -168,6 +178,7 @@ _GEN = {
     "rmsnorm": rmsnorm_inputs,
     "layernorm": layernorm_inputs,
     "cross_entropy": cross_entropy_inputs,
+    "add_layernorm": add_layernorm_inputs,
 }
 
 

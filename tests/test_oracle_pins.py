@@ -232,6 +232,86 @@ def test_layernorm_brute_force_tiny(n):
 
 
 # --------------------------------------------------------------------------
+# fused residual LayerNorm
+# --------------------------------------------------------------------------
+
+def _res_inputs(rows, cols, seed=11):
+    d = synth.add_layernorm_inputs(rows, cols, seed=seed)
+    return d["x"], d["residual"], d["gamma"], d["beta"]
+
+
+def test_add_layernorm_zero_residual_is_layernorm():
+    # x + 0.0f == x exactly, so the fused op must equal LayerNorm of x bit for bit
+    x, _, g, b = _res_inputs(4, 1537)
+    z = np.zeros_like(x)
+    assert np.array_equal(oracle.add_layernorm(x, z, g, b, 1e-5), oracle.layernorm(x, g, b, 1e-5))
+
+
+def test_add_layernorm_is_symmetric_in_its_inputs():
+    x, r, g, b = _res_inputs(3, 1000)
+    assert np.array_equal(oracle.add_layernorm(x, r, g, b, 1e-5), oracle.add_layernorm(r, x, g, b, 1e-5))
+
+
+def test_add_layernorm_combined_is_float32_sum():
+    # the combined tensor is one IEEE single-precision addition per element
+    x, r, g, b = _res_inputs(3, 777)
+    _, s = oracle.add_layernorm(x, r, g, b, 1e-5, with_sum=True)
+    assert s.dtype == np.float32
+    assert np.array_equal(s, np.add(x, r, dtype=np.float32))
+    # and it differs from the exact (double) sum somewhere, so the FP32 rounding is observable
+    assert not np.array_equal(s.astype(np.float64), x.astype(np.float64) + r.astype(np.float64))
+
+
+def test_add_layernorm_reduces_to_numpy_standardisation_of_fp32_sum():
+    x, r, g, b = _res_inputs(4, 6144)
+    c = np.add(x, r, dtype=np.float32).astype(np.float64)
+    eps = oracle.eps_as_f32(1e-5)
+    ref = (c - c.mean(axis=1, keepdims=True)) / np.sqrt(c.var(axis=1, keepdims=True) + eps)
+    ref = ref * g.astype(np.float64) + b.astype(np.float64)
+    np.testing.assert_allclose(oracle.add_layernorm(x, r, g, b, 1e-5), ref, rtol=1e-11, atol=1e-12)
+    # the double-precision sum is a different (rejected) reading: it moves outputs by ~1e-7
+    exact = x.astype(np.float64) + r.astype(np.float64)
+    ref2 = (exact - exact.mean(axis=1, keepdims=True)) / np.sqrt(exact.var(axis=1, keepdims=True) + eps)
+    ref2 = ref2 * g.astype(np.float64) + b.astype(np.float64)
+    assert np.abs(ref2 - ref).max() > 1e-9
+
+
+def test_add_layernorm_constant_combination_is_beta():
+    # dyadic x and c - x are exact in FP32, so every combined value is c: y = beta exactly
+    rng = np.random.default_rng(5)
+    x = (rng.integers(-1024, 1025, size=(3, 129)) / 64.0).astype(np.float32)
+    r = (np.float32(7.5) - x).astype(np.float32)
+    g = synth.uniform_f32(0, 1, 129, 0.5, 1.5)
+    b = synth.normal_f32(0, 2, 129, 0.0, 0.1)
+    assert np.array_equal(oracle.add_layernorm(x, r, g, b, 1e-5), np.tile(b.astype(np.float64), (3, 1)))
+
+
+def test_add_layernorm_mean_zero_variance_closed_form():
+    x, r, _, _ = _res_inputs(3, 2049)
+    c = np.add(x, r, dtype=np.float32).astype(np.float64)
+    v = np.var(c, axis=1)
+    e = oracle.eps_as_f32(1e-5)
+    y = oracle.add_layernorm(x, r, None, None, 1e-5)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose(np.var(y, axis=1), v / (v + e), rtol=1e-12)
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 64, 257])
+def test_add_layernorm_brute_force_tiny(n):
+    x, r, g, b = _res_inputs(2, n, seed=300 + n)
+    eps = oracle.eps_as_f32(1e-5)
+    y = oracle.add_layernorm(x, r, g, b, 1e-5)
+    for i in range(2):
+        row = [float(np.float32(x[i, j]) + np.float32(r[i, j])) for j in range(n)]
+        mu = math.fsum(row) / n
+        var = math.fsum((v - mu) ** 2 for v in row) / n
+        d = math.sqrt(var + eps)
+        for j in range(n):
+            assert y[i, j] == pytest.approx((row[j] - mu) / d * float(g[j]) + float(b[j]),
+                                            rel=1e-12, abs=1e-13)
+
+
+# --------------------------------------------------------------------------
 # cross-entropy
 # --------------------------------------------------------------------------
 
