@@ -250,6 +250,7 @@ def main():
                 torch.cuda.synchronize()
                 us = a.elapsed_time(z) * 1e3 / n
                 extra[f"{op}_768x6144_warm"] = {"us_per_op": round(us, 3), "gbps": round(b / us / 1e3, 1)}
+        extra.update(add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets))
         ce = synth.cross_entropy_inputs(4096, 32000, seed=0)
         cx = [torch.from_numpy(ce["logits"]).to(dev)]
         cx.append(cx[0].clone())
@@ -291,6 +292,47 @@ def main():
         out["cpu_baseline"] = cpu_baseline(soft, rms, ln, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets) -> dict:
+    """Fused residual LayerNorm 768x6144 (x, residual, gamma, beta in; y out,
+    with and without the combined output), rotating buffer sets as the step."""
+    inp = synth.add_layernorm_inputs(ROWS, COLS, seed=0)
+    x0 = torch.from_numpy(inp["x"]).to(dev)
+    r0 = torch.from_numpy(inp["residual"]).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    rs = [r0] + [r0.clone() for _ in range(nsets - 1)]
+    ys = [torch.empty_like(x0) for _ in range(nsets)]
+    ss = [torch.empty_like(x0) for _ in range(nsets)]
+    g = torch.from_numpy(inp["gamma"]).to(dev)
+    b = torch.from_numpy(inp["beta"]).to(dev)
+    out = {}
+    n = 400
+    tb = ROWS * COLS * 4
+    for with_sum in (False, True):
+        def launch(i):
+            k = i % nsets
+            st = lr.lib.lr_add_layernorm_f32(xs[k].data_ptr(), rs[k].data_ptr(), g.data_ptr(), b.data_ptr(),
+                                             ys[k].data_ptr(), ss[k].data_ptr() if with_sum else None,
+                                             ROWS, COLS, EPS["layernorm"], 0, sh)
+            if st != 0:
+                raise lr.LrError(st, "add_layernorm")
+        for i in range(20):
+            launch(i)
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            launch(i)
+        z.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(z) * 1e3 / n
+        moved = (4 if with_sum else 3) * tb
+        key = "add_layernorm_768x6144_cold" + ("_with_sum" if with_sum else "")
+        out[key] = {"us_per_op": round(us, 3), "gbps": round(moved / us / 1e3, 1),
+                    "pct_of_hbm_peak": round(100 * moved / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": moved}
+    del xs, rs, ys, ss
+    return out
 
 
 def _cpu_model() -> str:

@@ -75,7 +75,8 @@ typedef enum lr_op {
     LR_OP_SOFTMAX = 0,
     LR_OP_RMSNORM = 1,
     LR_OP_LAYERNORM = 2,
-    LR_OP_CROSS_ENTROPY = 3
+    LR_OP_CROSS_ENTROPY = 3,
+    LR_OP_ADD_LAYERNORM = 4
 } lr_op;
 
 /* Kernel families.
@@ -162,7 +163,25 @@ lr_status lr_cross_entropy_f32(const float* logits, const int64_t* labels,
                                float* losses, int64_t rows, int64_t cols,
                                lr_reduction_policy policy, hipStream_t stream);
 
-/* The same four operations under an explicit plan (the pages' exact
+/* Fused residual LayerNorm ("TIRx Metal reduction lowering", section 5.1:
+ * combined = X + residual, then the two-pass LayerNorm of combined; each
+ * input element is read from memory once):
+ *   c[r][j] = x[r][j] + residual[r][j]      (one FP32 addition)
+ *   mu = sum_k c/cols;  var = sum_k (c - mu)^2 / cols;
+ *   y = (c - mu) / sqrt(var + eps) * gamma + beta.
+ * x, residual: rows*cols FP32 in.  gamma, beta: cols FP32 each, or NULL for
+ * 1 / 0 (NULL, NULL is the pages' program).  y: rows*cols FP32 out.
+ * sum_out: rows*cols FP32 out receiving c, or NULL (not written).
+ * Aliasing: y may be exactly x or exactly residual, and so may sum_out; y and
+ * sum_out must not overlap each other or gamma/beta (else LR_ERR_ALIASING).
+ * Under LR_ORDERED_FOLD the statistics are the left folds of LayerNorm taken
+ * over c.  Errors as for lr_layernorm_f32; residual is required. */
+lr_status lr_add_layernorm_f32(const float* x, const float* residual, const float* gamma,
+                               const float* beta, float* y, float* sum_out, int64_t rows,
+                               int64_t cols, float eps, lr_reduction_policy policy,
+                               hipStream_t stream);
+
+/* The same operations under an explicit plan (the pages' exact
  * thread/packing constraints, section 6: honoured exactly or rejected).
  * `plan->family` must be LR_FAMILY_ORDERED exactly when policy is
  * LR_ORDERED_FOLD.  A plan that does not cover the row, exceeds a device
@@ -181,6 +200,11 @@ lr_status lr_layernorm_f32_with_plan(const float* x, const float* gamma, const f
                                      hipStream_t stream);
 lr_status lr_cross_entropy_f32_with_plan(const float* logits, const int64_t* labels,
                                          float* losses, int64_t rows, int64_t cols,
+                                         lr_reduction_policy policy, const lr_plan* plan,
+                                         hipStream_t stream);
+lr_status lr_add_layernorm_f32_with_plan(const float* x, const float* residual,
+                                         const float* gamma, const float* beta, float* y,
+                                         float* sum_out, int64_t rows, int64_t cols, float eps,
                                          lr_reduction_policy policy, const lr_plan* plan,
                                          hipStream_t stream);
 

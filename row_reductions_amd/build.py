@@ -41,6 +41,7 @@ SOURCES = [
     "k_rmsnorm.hip",
     "k_layernorm.hip",
     "k_cross_entropy.hip",
+    "k_add_layernorm.hip",
     "k_ordered.hip",
 ]
 

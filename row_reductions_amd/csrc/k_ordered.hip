@@ -40,16 +40,22 @@ __device__ __forceinline__ float contrib(float x, float ref) {
     return expf(x - ref);  // kExpShift: ref is the row maximum
 }
 
+// Element j of the row: x_j, or the FP32 sum x_j + residual_j when the row
+// is the fused residual LayerNorm's combined input (rr not null).
+__device__ __forceinline__ float row_elem(const float* xr, const float* rr, int e) {
+    return rr ? xr[e] + rr[e] : xr[e];
+}
+
 // acc_{j+1} = acc_j + c(x_j), j = 0 .. cols-1, in FP32, identical in all lanes.
 template <int C>
-__device__ float ordered_fold(const float* xr, int cols, float ref, float* slab, int lane) {
+__device__ float ordered_fold(const float* xr, const float* rr, int cols, float ref, float* slab, int lane) {
     float acc = 0.0f;
     for (int base = 0; base < cols; base += kSlab) {
         const int slab_id = base / kSlab;
 #pragma unroll
         for (int i = 0; i < kSlab / kWave; ++i) {
             const int e = ordered_elem(slab_id, i, lane);
-            if (e < cols) slab[kWave * i + lane] = contrib<C>(xr[e], ref);
+            if (e < cols) slab[kWave * i + lane] = contrib<C>(row_elem(xr, rr, e), ref);
         }
         wave_sync();
         const int n = min(kSlab, cols - base);
@@ -83,7 +89,7 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
         float m = -INFINITY;
         for (int e = lane; e < cols; e += kWave) m = fmaxf(m, xr[e]);
         m = wave_allreduce<MaxOp>(m);
-        const float s = ordered_fold<kExpShift>(xr, cols, m, slab, lane);
+        const float s = ordered_fold<kExpShift>(xr, nullptr, cols, m, slab, lane);
         if constexpr (OP == kCrossEntropy) {
             if (lane == 0) {
                 const int64_t lab = a.labels[row];
@@ -95,7 +101,7 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
             for (int e = lane; e < cols; e += kWave) yr[e] = expf(xr[e] - m) / s;
         }
     } else if constexpr (OP == kRmsNorm) {
-        const float ss = ordered_fold<kSquare>(xr, cols, 0.0f, slab, lane);
+        const float ss = ordered_fold<kSquare>(xr, nullptr, cols, 0.0f, slab, lane);
         const float ms = ss / n;
         const float r = 1.0f / sqrtf(ms + a.eps);
         float* yr = a.y + row * (int64_t)cols;
@@ -103,16 +109,22 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
             const float t = xr[e] * r;
             yr[e] = a.gamma ? t * a.gamma[e] : t;
         }
-    } else {  // kLayerNorm
-        const float mu = ordered_fold<kValue>(xr, cols, 0.0f, slab, lane) / n;
-        const float var = ordered_fold<kCentredSquare>(xr, cols, mu, slab, lane) / n;
+    } else {  // LayerNorm; fused residual LayerNorm folds over x + residual
+        const float* rr = OP == kAddLayerNorm ? a.residual + row * (int64_t)cols : nullptr;
+        const float mu = ordered_fold<kValue>(xr, rr, cols, 0.0f, slab, lane) / n;
+        const float var = ordered_fold<kCentredSquare>(xr, rr, cols, mu, slab, lane) / n;
         const float r = 1.0f / sqrtf(var + a.eps);
         float* yr = a.y + row * (int64_t)cols;
+        float* sr = (OP == kAddLayerNorm && a.sum_out) ? a.sum_out + row * (int64_t)cols : nullptr;
         for (int e = lane; e < cols; e += kWave) {
-            float t = (xr[e] - mu) * r;
+            // every read of element e precedes its writes (y or the sum may be
+            // x or the residual itself)
+            const float c = row_elem(xr, rr, e);
+            float t = (c - mu) * r;
             if (a.gamma) t = t * a.gamma[e];
             if (a.beta) t = t + a.beta[e];
             yr[e] = t;
+            if (sr) sr[e] = c;
         }
     }
 }
@@ -124,6 +136,7 @@ hipError_t launch_ordered(int op, const KArgs& a, const lr_plan& p, hipStream_t 
         case kRmsNorm: hipLaunchKernelGGL(k_ordered<kRmsNorm>, grid, block, 0, s, a); break;
         case kLayerNorm: hipLaunchKernelGGL(k_ordered<kLayerNorm>, grid, block, 0, s, a); break;
         case kCrossEntropy: hipLaunchKernelGGL(k_ordered<kCrossEntropy>, grid, block, 0, s, a); break;
+        case kAddLayerNorm: hipLaunchKernelGGL(k_ordered<kAddLayerNorm>, grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -69,20 +69,26 @@ struct Call {
     int64_t cols;
     float eps;
     int policy;
+    const float* residual = nullptr;  // fused residual LayerNorm
+    float* sum_out = nullptr;         // fused residual LayerNorm, optional
 };
 
 lr_status validate_call(const Call& c) {
     if (c.policy != LR_UNORDERED_TREE && c.policy != LR_ORDERED_FOLD) return LR_ERR_INVALID_POLICY;
     const bool ce = c.op == LR_OP_CROSS_ENTROPY;
+    const bool res = c.op == LR_OP_ADD_LAYERNORM;
     if (c.x == nullptr) return LR_ERR_NULL_POINTER;
     if (ce ? (c.labels == nullptr || c.losses == nullptr) : c.y == nullptr) return LR_ERR_NULL_POINTER;
+    if (res && c.residual == nullptr) return LR_ERR_NULL_POINTER;
     if (c.rows < 0 || c.cols < 1 || c.cols >= (int64_t(1) << 24) || c.rows > INT32_MAX) return LR_ERR_INVALID_SHAPE;
     if (c.rows > INT64_MAX / 4 / c.cols) return LR_ERR_INVALID_SHAPE;
-    if (c.op == LR_OP_RMSNORM || c.op == LR_OP_LAYERNORM) {
+    if (c.op == LR_OP_RMSNORM || c.op == LR_OP_LAYERNORM || res) {
         if (!std::isfinite(c.eps) || c.eps < 0.0f) return LR_ERR_INVALID_EPS;
     }
     auto a4 = [](const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
-    if (!a4(c.x) || !a4(c.y) || !a4(c.gamma) || !a4(c.beta) || !a4(c.losses)) return LR_ERR_MISALIGNED;
+    if (!a4(c.x) || !a4(c.y) || !a4(c.gamma) || !a4(c.beta) || !a4(c.losses) || !a4(c.residual) ||
+        !a4(c.sum_out))
+        return LR_ERR_MISALIGNED;
     if (c.labels != nullptr && (reinterpret_cast<uintptr_t>(c.labels) & 7u) != 0) return LR_ERR_MISALIGNED;
     const int64_t tb = c.rows * c.cols * 4;
     const Range rx = range_of(c.x, tb);
@@ -90,10 +96,22 @@ lr_status validate_call(const Call& c) {
         const Range rl = range_of(c.losses, c.rows * 4), rlab = range_of(c.labels, c.rows * 8);
         if (c.rows > 0 && (overlap(rl, rx) || overlap(rl, rlab))) return LR_ERR_ALIASING;
     } else if (c.rows > 0) {
-        const Range ry = range_of(c.y, tb);
-        if (c.y != c.x && overlap(ry, rx)) return LR_ERR_ALIASING;
-        if (c.gamma != nullptr && overlap(ry, range_of(c.gamma, c.cols * 4))) return LR_ERR_ALIASING;
-        if (c.beta != nullptr && overlap(ry, range_of(c.beta, c.cols * 4))) return LR_ERR_ALIASING;
+        // an output may be exactly one of the row inputs (in place); any other
+        // overlap with an input, or between the two outputs, is rejected
+        auto apart_or_same = [&](const float* o, const float* in) {
+            return o == in || !overlap(range_of(o, tb), range_of(in, tb));
+        };
+        auto output_ok = [&](const float* o) {
+            const Range ro = range_of(o, tb);
+            if (!apart_or_same(o, c.x)) return false;
+            if (res && !apart_or_same(o, c.residual)) return false;
+            if (c.gamma != nullptr && overlap(ro, range_of(c.gamma, c.cols * 4))) return false;
+            if (c.beta != nullptr && overlap(ro, range_of(c.beta, c.cols * 4))) return false;
+            return true;
+        };
+        if (!output_ok(c.y)) return LR_ERR_ALIASING;
+        if (c.sum_out != nullptr && (!output_ok(c.sum_out) || overlap(range_of(c.sum_out, tb), range_of(c.y, tb))))
+            return LR_ERR_ALIASING;
     }
     return LR_OK;
 }
@@ -104,7 +122,8 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     if (c.rows == 0) return LR_OK;  // nothing to launch
     const bool ce = c.op == LR_OP_CROSS_ENTROPY;
     const bool rows_aligned = c.cols % kVec == 0 && aligned16(c.x);
-    const bool aligned = rows_aligned && (ce || (aligned16(c.y) && aligned16(c.gamma) && aligned16(c.beta)));
+    const bool aligned = rows_aligned && (ce || (aligned16(c.y) && aligned16(c.gamma) && aligned16(c.beta) &&
+                                                 aligned16(c.residual) && aligned16(c.sum_out)));
 
     lr_device_facts facts;
     st = current_facts(&facts);
@@ -134,9 +153,16 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     a.S = plan.waves_per_row;
     a.Q = plan.rows_per_block;
     a.team_magic = team_magic(plan.waves_per_row);
-    a.y_same_phase = ce ? 1
-                        : (int32_t)((reinterpret_cast<uintptr_t>(c.y) & 15u) ==
-                                    (reinterpret_cast<uintptr_t>(c.x) & 15u));
+    auto same_phase = [&](const void* p) {
+        return p == nullptr ? 1
+                            : (int32_t)((reinterpret_cast<uintptr_t>(p) & 15u) ==
+                                        (reinterpret_cast<uintptr_t>(c.x) & 15u));
+    };
+    a.y_same_phase = ce ? 1 : same_phase(c.y);
+    a.residual = c.residual;
+    a.sum_out = c.sum_out;
+    a.r_same_phase = same_phase(c.residual);
+    a.s_same_phase = same_phase(c.sum_out);
 
     (void)hipGetLastError();  // clear a stale error so the launch's own status is seen
     hipError_t e;
@@ -147,6 +173,7 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
             case LR_OP_SOFTMAX: e = launch_softmax(a, plan, aligned, stream); break;
             case LR_OP_RMSNORM: e = launch_rmsnorm(a, plan, aligned, stream); break;
             case LR_OP_LAYERNORM: e = launch_layernorm(a, plan, aligned, stream); break;
+            case LR_OP_ADD_LAYERNORM: e = launch_add_layernorm(a, plan, aligned, stream); break;
             default: e = launch_cross_entropy(a, plan, aligned, stream); break;
         }
     }
@@ -185,6 +212,15 @@ lr_status lr_cross_entropy_f32(const float* logits, const int64_t* labels, float
         nullptr, stream);
 }
 
+lr_status lr_add_layernorm_f32(const float* x, const float* residual, const float* gamma, const float* beta,
+                               float* y, float* sum_out, int64_t rows, int64_t cols, float eps,
+                               lr_reduction_policy policy, hipStream_t stream) {
+    Call c{LR_OP_ADD_LAYERNORM, x, gamma, beta, y, nullptr, nullptr, rows, cols, eps, policy};
+    c.residual = residual;
+    c.sum_out = sum_out;
+    return lr::run(c, nullptr, stream);
+}
+
 static lr_status need_plan(const lr_plan* plan) { return plan == nullptr ? LR_ERR_NULL_POINTER : LR_OK; }
 
 lr_status lr_softmax_f32_with_plan(const float* x, float* y, int64_t rows, int64_t cols,
@@ -217,6 +253,17 @@ lr_status lr_cross_entropy_f32_with_plan(const float* logits, const int64_t* lab
     return lr::run(
         Call{LR_OP_CROSS_ENTROPY, logits, nullptr, nullptr, nullptr, labels, losses, rows, cols, 0.0f, policy},
         plan, stream);
+}
+
+lr_status lr_add_layernorm_f32_with_plan(const float* x, const float* residual, const float* gamma,
+                                         const float* beta, float* y, float* sum_out, int64_t rows,
+                                         int64_t cols, float eps, lr_reduction_policy policy,
+                                         const lr_plan* plan, hipStream_t stream) {
+    if (need_plan(plan) != LR_OK) return LR_ERR_NULL_POINTER;
+    Call c{LR_OP_ADD_LAYERNORM, x, gamma, beta, y, nullptr, nullptr, rows, cols, eps, policy};
+    c.residual = residual;
+    c.sum_out = sum_out;
+    return lr::run(c, plan, stream);
 }
 
 lr_status lr_device_facts_query(lr_device_facts* out) {

@@ -9,7 +9,10 @@
 
 namespace lr {
 
-enum Op : int { kSoftmax = 0, kRmsNorm = 1, kLayerNorm = 2, kCrossEntropy = 3 };
+enum Op : int { kSoftmax = 0, kRmsNorm = 1, kLayerNorm = 2, kCrossEntropy = 3, kAddLayerNorm = 4 };
+
+// LayerNorm statistics (mean, then centred variance) with a per-column affine.
+constexpr bool is_layernorm(int op) { return op == kLayerNorm || op == kAddLayerNorm; }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

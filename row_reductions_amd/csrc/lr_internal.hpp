@@ -25,6 +25,10 @@ struct KArgs {
     int32_t Q;              // rows per workgroup
     int32_t y_same_phase;   // y rows start at the same 16-byte phase as x rows
     int32_t team_magic;     // team_magic(S): wave index / S as a multiply
+    const float* residual;  // fused residual LayerNorm: second input, else null
+    float* sum_out;         // fused residual LayerNorm: x + residual out, or null
+    int32_t r_same_phase;   // residual rows start at the same 16-byte phase as x rows
+    int32_t s_same_phase;   // sum_out rows start at the same 16-byte phase as x rows
 };
 
 // Compiled cache-family chunk counts (chunks_per_lane), ascending.
@@ -44,6 +48,7 @@ hipError_t launch_softmax(const KArgs& a, const lr_plan& p, bool aligned, hipStr
 hipError_t launch_rmsnorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_cross_entropy(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_add_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_ordered(int op, const KArgs& a, const lr_plan& p, hipStream_t s);
 
 }  // namespace lr

@@ -29,20 +29,35 @@ __device__ __forceinline__ float gather_label(const KArgs& a, const float* xr, i
     return (lab >= 0 && lab < (int64_t)a.cols) ? xr[lab] : 0.0f;
 }
 
-// Stores out, the values of chunk k of row yr (x-row phase h).
+// Stores out, the values of chunk k of the x row's grid (phase h), into the
+// destination row dr.  `same_phase`: dr starts at the x row's 16-byte phase,
+// so whole chunks can be stored as one 128-bit access.
 template <bool AL>
-__device__ __forceinline__ void store_chunk(const KArgs& a, float* yr, int k, int h, float4 out) {
+__device__ __forceinline__ void store_chunk(float* dr, bool same_phase, int k, int h, int cols, float4 out) {
     if (AL) {
-        st4(reinterpret_cast<float4*>(yr) + k, out);
-    } else if (a.y_same_phase && chunk_full(k, h, a.cols)) {
-        st4(reinterpret_cast<float4*>(yr - h) + k, out);
+        st4(reinterpret_cast<float4*>(dr) + k, out);
+    } else if (same_phase && chunk_full(k, h, cols)) {
+        st4(reinterpret_cast<float4*>(dr - h) + k, out);
     } else {
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
             const int e = elem_index(k, j, h);
-            if (elem_valid(e, a.cols)) yr[e] = get(out, j);
+            if (elem_valid(e, cols)) dr[e] = get(out, j);
         }
     }
+}
+
+// Chunk k of a row that sits at its own (unknown) phase, read one float at a
+// time at clamped, in-range indexes of the x row's grid (phase h); grid slots
+// outside [0, cols) hold some element of the row and must not be used.
+__device__ __forceinline__ float4 elem_chunk(BufRes r, int k, int h, int cols) {
+    float4 g;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+        const int e = min(max(elem_index(k, j, h), 0), cols - 1);
+        set(g, j, res_ld1(r, e * 4));
+    }
+    return g;
 }
 
 // Per-column parameter (gamma or beta) for chunk k; `fill` where absent.
@@ -81,11 +96,7 @@ __device__ __forceinline__ float4 param_load(BufRes r, bool present, int k, int 
         if constexpr (AL) {
             g = res_ld4<kAuxDefault>(r, k * 16);
         } else {
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) {
-                const int e = min(max(elem_index(k, j, h), 0), cols - 1);
-                set(g, j, res_ld1(r, e * 4));
-            }
+            g = elem_chunk(r, k, h, cols);
         }
         if constexpr (PM == kParRuntime) {
             if (!present) g = splat4(fill);
@@ -97,7 +108,7 @@ __device__ __forceinline__ float4 param_load(BufRes r, bool present, int k, int 
 // Parameters of a norm (gamma; gamma and beta for LayerNorm).
 template <int OP>
 constexpr int num_params() {
-    return OP == kLayerNorm ? 2 : (OP == kRmsNorm ? 1 : 0);
+    return is_layernorm(OP) ? 2 : (OP == kRmsNorm ? 1 : 0);
 }
 
 // Wave index within the workgroup, as a scalar (uniform) value.
@@ -137,13 +148,22 @@ k_cache(const KArgs a) {
     const BufRes rx = make_res(xr - h, nv * 16);
     const BufRes rg = make_res(a.gamma, NP >= 1 && a.gamma ? cols * 4 : 0);
     const BufRes rb = make_res(a.beta, NP == 2 && a.beta ? cols * 4 : 0);
+    // fused residual: aligned rows read it on the x grid, misaligned rows one
+    // float at a time (its phase need not match x's)
+    constexpr bool RES = OP == kAddLayerNorm;
+    const int64_t roff = (active ? row : 0) * (int64_t)cols;
+    const BufRes rr = make_res(RES ? a.residual + roff : nullptr, RES && active ? (AL ? nv * 16 : cols * 4) : 0);
     auto chunk = [&](int c) { return chunk_index(t.w, W, c); };
 
     float4 v[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int k = chunk(c);
-        const float4 raw = res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rx, k * 16);
+        float4 raw = res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rx, k * 16);
+        if constexpr (RES) {
+            const float4 q = AL ? res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rr, k * 16) : elem_chunk(rr, k, h, cols);
+            raw = make_float4(raw.x + q.x, raw.y + q.y, raw.z + q.z, raw.w + q.w);
+        }
         if constexpr (ID == 0.0f && AL) {
             v[c] = raw;  // past the end: zeros, the add identity
         } else {
@@ -182,7 +202,7 @@ k_cache(const KArgs a) {
                 const int k = chunk(c);
                 if (k < nv) {
                     const float4 o = make_float4(v[c].x * r, v[c].y * r, v[c].z * r, v[c].w * r);
-                    store_chunk<AL>(a, yr, k, h, o);
+                    store_chunk<AL>(yr, a.y_same_phase, k, h, cols, o);
                 }
             }
         }
@@ -201,13 +221,23 @@ k_cache(const KArgs a) {
                 const float4 g = param_load<AL, PM>(rg, a.gamma != nullptr, k, h, cols, 1.0f);
                 const float4 o = make_float4(v[c].x * r * g.x, v[c].y * r * g.y,
                                              v[c].z * r * g.z, v[c].w * r * g.w);
-                store_chunk<AL>(a, yr, k, h, o);
+                store_chunk<AL>(yr, a.y_same_phase, k, h, cols, o);
             }
         }
-    } else {  // kLayerNorm
+    } else {  // LayerNorm, fused residual LayerNorm
         float sum = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) sum += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+        if constexpr (RES) {
+            if (a.sum_out != nullptr) {
+                float* sr = a.sum_out + row * (int64_t)cols;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const int k = chunk(c);
+                    if (k < nv) store_chunk<AL>(sr, a.s_same_phase, k, h, cols, v[c]);
+                }
+            }
+        }
         sum = team_reduce<AddOp>(sum, red[0], S, t);
         const float mu = sum * a.inv_cols;
         float qs = 0.0f;
@@ -231,7 +261,7 @@ k_cache(const KArgs a) {
                 const float4 b = param_load<AL, PM>(rb, a.beta != nullptr, k, h, cols, 0.0f);
                 const float4 o = make_float4(v[c].x * r * g.x + b.x, v[c].y * r * g.y + b.y,
                                              v[c].z * r * g.z + b.z, v[c].w * r * g.w + b.w);
-                store_chunk<AL>(a, yr, k, h, o);
+                store_chunk<AL>(yr, a.y_same_phase, k, h, cols, o);
             }
         }
     }
@@ -243,12 +273,16 @@ k_cache(const KArgs a) {
 // sum of exp) online in one pass and merge the per-worker pairs at the end.
 // ===========================================================================
 template <int OP, bool AL>
-__device__ __forceinline__ void load_trip(float4 (&v)[kStreamUnroll], const float4* xa, int k0,
+__device__ __forceinline__ void load_trip(float4 (&v)[kStreamUnroll], const float4* xa, BufRes rr, int k0,
                                           int W, int nv, int h, int cols, float id) {
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) {
         const int k = k0 + W * u;
         v[u] = (k < nv) ? ld4(xa + k) : splat4(id);
+        if constexpr (OP == kAddLayerNorm) {  // + residual (FP32); id is 0
+            const float4 q = AL ? res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rr, k * 16) : elem_chunk(rr, k, h, cols);
+            if (k < nv) v[u] = make_float4(v[u].x + q.x, v[u].y + q.y, v[u].z + q.z, v[u].w + q.w);
+        }
         if (!AL) mask_chunk(v[u], k, h, cols, id);
     }
 }
@@ -269,6 +303,9 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
     const int nv = active ? (AL ? cols / kVec : chunks_of(h, cols)) : 0;
     const float4* xa = reinterpret_cast<const float4*>(xr - h);
     float* yr = a.y + (active ? row : 0) * (int64_t)cols;
+    const int64_t roff = (active ? row : 0) * (int64_t)cols;
+    const BufRes rr = make_res(OP == kAddLayerNorm ? a.residual + roff : nullptr,
+                               OP == kAddLayerNorm && active ? (AL ? nv * 16 : cols * 4) : 0);
 
     float sel = 0.0f;
     if constexpr (OP == kCrossEntropy) {
@@ -279,7 +316,7 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
         float m = -INFINITY, s = 0.0f;
         for (int k0 = t.w; k0 < nv; k0 += W * U) {
             float4 v[U];
-            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+            load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
             float tm = m;
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -301,14 +338,14 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
             const float r = fast_rcp(tot);
             for (int k0 = t.w; k0 < nv; k0 += W * U) {
                 float4 v[U];
-                load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+                load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int k = k0 + W * u;
                     if (k < nv) {
                         const float4 o = make_float4(fast_exp(v[u].x - M) * r, fast_exp(v[u].y - M) * r,
                                                      fast_exp(v[u].z - M) * r, fast_exp(v[u].w - M) * r);
-                        store_chunk<AL>(a, yr, k, h, o);
+                        store_chunk<AL>(yr, a.y_same_phase, k, h, cols, o);
                     }
                 }
             }
@@ -317,7 +354,7 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
         float ss = 0.0f;
         for (int k0 = t.w; k0 < nv; k0 += W * U) {
             float4 v[U];
-            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+            load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 ss += (v[u].x * v[u].x + v[u].y * v[u].y) + (v[u].z * v[u].z + v[u].w * v[u].w);
@@ -326,7 +363,7 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
         const float r = fast_rsqrt(ss * a.inv_cols + a.eps);
         for (int k0 = t.w; k0 < nv; k0 += W * U) {
             float4 v[U];
-            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+            load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + W * u;
@@ -334,15 +371,15 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
                     const float4 g = param_chunk<AL>(a.gamma, k, h, cols, 1.0f);
                     const float4 o = make_float4(v[u].x * r * g.x, v[u].y * r * g.y,
                                                  v[u].z * r * g.z, v[u].w * r * g.w);
-                    store_chunk<AL>(a, yr, k, h, o);
+                    store_chunk<AL>(yr, a.y_same_phase, k, h, cols, o);
                 }
             }
         }
-    } else {  // kLayerNorm
+    } else {  // LayerNorm, fused residual LayerNorm
         float sum = 0.0f;
         for (int k0 = t.w; k0 < nv; k0 += W * U) {
             float4 v[U];
-            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+            load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
 #pragma unroll
             for (int u = 0; u < U; ++u) sum += (v[u].x + v[u].y) + (v[u].z + v[u].w);
         }
@@ -351,7 +388,7 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
         float qs = 0.0f;
         for (int k0 = t.w; k0 < nv; k0 += W * U) {
             float4 v[U];
-            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+            load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + W * u;
@@ -365,7 +402,7 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
         const float r = fast_rsqrt(qs * a.inv_cols + a.eps);
         for (int k0 = t.w; k0 < nv; k0 += W * U) {
             float4 v[U];
-            load_trip<OP, AL>(v, xa, k0, W, nv, h, cols, ID);
+            load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + W * u;
@@ -374,7 +411,11 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
                     const float4 b = param_chunk<AL>(a.beta, k, h, cols, 0.0f);
                     const float4 o = make_float4((v[u].x - mu) * r * g.x + b.x, (v[u].y - mu) * r * g.y + b.y,
                                                  (v[u].z - mu) * r * g.z + b.z, (v[u].w - mu) * r * g.w + b.w);
-                    store_chunk<AL>(a, yr, k, h, o);
+                    store_chunk<AL>(yr, a.y_same_phase, k, h, cols, o);
+                    // the sum is written in this last pass only, so an output
+                    // that is x or the residual itself is not read after it
+                    if (OP == kAddLayerNorm && a.sum_out != nullptr)
+                        store_chunk<AL>(a.sum_out + roff, a.s_same_phase, k, h, cols, v[u]);
                 }
             }
         }

@@ -24,7 +24,7 @@ import torch
 import row_reductions_amd as lr
 
 
-def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh):
+def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh, rs=None):
     pol = lr._policy(policy)
 
     def run(i, plan):
@@ -35,6 +35,8 @@ def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh):
             return lr.lr_rmsnorm_f32(xs[k], g, ys[k], rows, cols, eps, pol, sh, plan)
         if op == "layernorm":
             return lr.lr_layernorm_f32(xs[k], g, b, ys[k], rows, cols, eps, pol, sh, plan)
+        if op == "add_layernorm":
+            return lr.lr_add_layernorm_f32(xs[k], rs[k], g, b, ys[k], None, rows, cols, eps, pol, sh, plan)
         return lr.lr_cross_entropy_f32(xs[k], lab, ys[k], rows, cols, pol, sh, plan)
     return run
 
@@ -82,7 +84,8 @@ def main(argv=None):
     g = torch.rand(cols, device=dev, generator=gen) + 0.5
     b = torch.randn(cols, device=dev, generator=gen) * 0.1
     lab = torch.randint(0, cols, (rows,), device=dev, generator=gen)
-    run = _launcher(op, xs, ys, g, b, lab, rows, cols, args.eps, args.policy, sh)
+    rs = [torch.randn(rows, cols, device=dev, generator=gen) for _ in range(sets)] if op == "add_layernorm" else None
+    run = _launcher(op, xs, ys, g, b, lab, rows, cols, args.eps, args.policy, sh, rs)
 
     facts = lr.lr_device_facts_query()
     aligned = 1 if cols % 4 == 0 else 0
@@ -107,14 +110,15 @@ def main(argv=None):
     results.sort(key=lambda t: t[0])
     best_us, best, _ = results[0]
     again = _time(run, best, args.iters, stream)
-    moved = 2 * tensor_bytes if op != "cross_entropy" else tensor_bytes + rows * 12
+    moved = {"cross_entropy": tensor_bytes + rows * 12, "add_layernorm": 3 * tensor_bytes}.get(op, 2 * tensor_bytes)
     print(f"# {op} {rows}x{cols} {args.policy}: {len(results)} candidates, "
           f"automatic {_time(run, auto, args.iters, stream):.2f} us, "
           f"best {again:.2f} us ({moved / again / 1e3:.0f} GB/s): {best!r}")
     for us, p, rec in results[:8]:
         print(f"#   {us:8.2f} us  {p!r}")
     fam = {0: "LR_FAMILY_CACHE", 1: "LR_FAMILY_STREAM", 2: "LR_FAMILY_ORDERED"}[best.family]
-    opn = {0: "LR_OP_SOFTMAX", 1: "LR_OP_RMSNORM", 2: "LR_OP_LAYERNORM", 3: "LR_OP_CROSS_ENTROPY"}[lr.OPS[op]]
+    opn = {0: "LR_OP_SOFTMAX", 1: "LR_OP_RMSNORM", 2: "LR_OP_LAYERNORM", 3: "LR_OP_CROSS_ENTROPY",
+           4: "LR_OP_ADD_LAYERNORM"}[lr.OPS[op]]
     pol = "LR_ORDERED_FOLD" if args.policy == "ordered_fold" else "LR_UNORDERED_TREE"
     print(f"{{{opn}, {pol}, {rows}, {cols}, {aligned}, {fam}, {best.waves_per_row}, "
           f"{best.rows_per_block}, {best.chunks_per_lane}}},")

@@ -18,6 +18,8 @@ G = 0x7F0020000000
 B = 0x7F0030000000
 LAB = 0x7F0040000000
 LOSS = 0x7F0050000000
+RES = 0x7F0060000000
+SUM = 0x7F0070000000
 
 
 def declared_functions():
@@ -42,6 +44,7 @@ def test_zero_rows_is_ok_without_launch():
     assert lr.lr_rmsnorm_f32(X, None, Y, 0, 5, 1e-6, 1, 0) == lr.LR_OK
     assert lr.lr_layernorm_f32(X, None, None, Y, 0, 7, 1e-5, 0, 0) == lr.LR_OK
     assert lr.lr_cross_entropy_f32(X, LAB, LOSS, 0, 32000, 0, 0) == lr.LR_OK
+    assert lr.lr_add_layernorm_f32(X, RES, None, None, Y, SUM, 0, 7, 1e-5, 0, 0) == lr.LR_OK
 
 
 @pytest.mark.parametrize("call,status", [
@@ -68,6 +71,21 @@ def test_zero_rows_is_ok_without_launch():
     (lambda: lr.lr_layernorm_f32(X, G, Y + 8, Y, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
     (lambda: lr.lr_cross_entropy_f32(X, LAB, X + 64, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
     (lambda: lr.lr_cross_entropy_f32(X, LAB, LAB + 8, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
+    # fused residual LayerNorm
+    (lambda: lr.lr_add_layernorm_f32(X, None, G, B, Y, None, 4, 8, 1e-5, 0, 0), lr.LR_ERR_NULL_POINTER),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, None, SUM, 4, 8, 1e-5, 0, 0), lr.LR_ERR_NULL_POINTER),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, SUM, 4, 8, float("nan"), 0, 0), lr.LR_ERR_INVALID_EPS),
+    (lambda: lr.lr_add_layernorm_f32(X, RES + 2, G, B, Y, SUM, 4, 8, 1e-5, 0, 0), lr.LR_ERR_MISALIGNED),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, SUM + 1, 4, 8, 1e-5, 0, 0), lr.LR_ERR_MISALIGNED),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, SUM, 4, 8, 1e-5, 3, 0), lr.LR_ERR_INVALID_POLICY),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, RES + 4, None, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, Y + 16, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, Y, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, X, X, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, Y + 8, B, Y, SUM, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, SUM + 8, Y, SUM, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
+    # y is x in place, but x and the residual overlap partially: rows would race
+    (lambda: lr.lr_add_layernorm_f32(X, X + 16, G, B, X, None, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
 ])
 def test_validation_status_before_any_hip_call(call, status):
     assert call() == status
@@ -84,3 +102,7 @@ def test_valid_call_without_device_reports_hip_error():
         pytest.skip("a GPU is present")
     assert lr.lr_softmax_f32(X, Y, 4, 8, 0, 0) == lr.LR_ERR_HIP
     assert lr.lr_softmax_f32(X, X, 4, 8, 0, 0) == lr.LR_ERR_HIP  # in place is allowed
+    # fused residual LayerNorm: outputs may be exactly x or the residual
+    assert lr.lr_add_layernorm_f32(X, RES, G, B, X, RES, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP
+    assert lr.lr_add_layernorm_f32(X, RES, None, None, RES, X, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP
+    assert lr.lr_add_layernorm_f32(X, X, None, None, Y, None, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP
