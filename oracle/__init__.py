@@ -51,6 +51,10 @@ def _load():
         lib.oracle_cross_entropy_f64.argtypes = [P, P, P, I64, I64]
         lib.oracle_add_layernorm_f64.argtypes = [P, P, P, P, P, P, I64, I64, ctypes.c_double]
         lib.oracle_add_layernorm_f64.restype = ctypes.c_int
+        lib.oracle_row_sum_f64.argtypes = [P, P, I64, I64]
+        lib.oracle_row_minmax_f32.argtypes = [P, P, P, I64, I64]
+        lib.oracle_row_sum_f64.restype = None
+        lib.oracle_row_minmax_f32.restype = None
         lib.oracle_rmsnorm_fold_f32.argtypes = [P, P, P, I64, I64, ctypes.c_float]
         lib.oracle_layernorm_fold_f32.argtypes = [P, P, P, P, I64, I64, ctypes.c_float]
         lib.oracle_fold_left_f32.argtypes = [P, I64, ctypes.c_int]
@@ -145,6 +149,23 @@ def cross_entropy(logits, labels) -> np.ndarray:
     out = np.empty(x.shape[0], dtype=np.float64)
     _load().oracle_cross_entropy_f64(_ptr(x), _ptr(lab), _ptr(out), x.shape[0], x.shape[1])
     return out
+
+
+def row_sum(x) -> np.ndarray:
+    """Per-row sum in double."""
+    x = _f32(x)
+    out = np.empty(x.shape[0], dtype=np.float64)
+    _load().oracle_row_sum_f64(_ptr(x), _ptr(out), x.shape[0], x.shape[1])
+    return out
+
+
+def row_minmax(x):
+    """Per-row (minimum, maximum), exact FP32 values."""
+    x = _f32(x)
+    lo = np.empty(x.shape[0], dtype=np.float32)
+    hi = np.empty(x.shape[0], dtype=np.float32)
+    _load().oracle_row_minmax_f32(_ptr(x), _ptr(lo), _ptr(hi), x.shape[0], x.shape[1])
+    return lo, hi
 
 
 def rmsnorm_fold_f32(x, gamma=None, eps: float = 1e-6) -> np.ndarray:

@@ -136,6 +136,33 @@ void oracle_cross_entropy_f64(const float* logits, const int64_t* labels,
     }
 }
 
+/* Row sum (the plain add reduction; section 8 of "TIRx Metal reduction
+ * lowering" checks row sums at widths 127, 257, 1024 and 4096):
+ * out[r] = sum_j x[r][j], accumulated in double. */
+void oracle_row_sum_f64(const float* x, double* out, int64_t rows, int64_t cols) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) s += (double)xr[j];
+        out[r] = s;
+    }
+}
+
+/* Row minimum and maximum together (section 8: minimum and maximum of each
+ * row in one pass, 7 x 1024).  Exact: both are input values. */
+void oracle_row_minmax_f32(const float* x, float* mins, float* maxs, int64_t rows, int64_t cols) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        float lo = xr[0], hi = xr[0];
+        for (int64_t j = 1; j < cols; ++j) {
+            if (xr[j] < lo) lo = xr[j];
+            if (xr[j] > hi) hi = xr[j];
+        }
+        if (mins != NULL) mins[r] = lo;
+        if (maxs != NULL) maxs[r] = hi;
+    }
+}
+
 /* ---------------------------------------------------------------------------
  * ordered_fold replay in FP32.  The pages' fold_left restriction (section 1
  * of "TIRx Metal reduction lowering") keeps a reduction as one ordered chain

@@ -62,6 +62,12 @@ void oracle_layernorm_stats_f64(const float* x, double* mean, double* var,
 void oracle_cross_entropy_f64(const float* logits, const int64_t* labels,
                               double* losses, int64_t rows, int64_t cols);
 
+/* out[r] = sum_j x[r][j]   (double) */
+void oracle_row_sum_f64(const float* x, double* out, int64_t rows, int64_t cols);
+
+/* mins[r] = min_j x[r][j], maxs[r] = max_j x[r][j] (exact; either may be NULL). */
+void oracle_row_minmax_f32(const float* x, float* mins, float* maxs, int64_t rows, int64_t cols);
+
 /* ordered_fold replay in FP32 (see above). */
 void oracle_rmsnorm_fold_f32(const float* x, const float* gamma, float* y,
                              int64_t rows, int64_t cols, float eps);

@@ -312,6 +312,60 @@ def test_add_layernorm_brute_force_tiny(n):
 
 
 # --------------------------------------------------------------------------
+# row sum, row minimum and maximum
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 3, 127, 257, 1024])
+def test_row_sum_brute_force_fsum(n):
+    x = _rand(4, n, seed=400 + n, mean=0.5, std=3.0)
+    got = oracle.row_sum(x)
+    for r in range(4):
+        row = [float(v) for v in x[r]]
+        exact = math.fsum(row)
+        # double accumulation of n terms: within n * 2^-53 * sum |x| of the exact sum
+        assert abs(got[r] - exact) <= n * 2.0 ** -53 * math.fsum(abs(v) for v in row) + 1e-300
+
+
+def test_row_sum_exact_cases():
+    # integers and dyadic values: every partial sum is exact
+    rng = np.random.default_rng(8)
+    k = rng.integers(-4096, 4097, size=(5, 4096))
+    x = (k / 8.0).astype(np.float32)
+    assert np.array_equal(oracle.row_sum(x), k.sum(axis=1) / 8.0)
+    assert np.array_equal(oracle.row_sum(np.ones((3, 257), np.float32)), np.full(3, 257.0))
+    # rows are independent and use stride cols
+    x = _rand(6, 129)
+    assert np.array_equal(oracle.row_sum(x)[2:5], oracle.row_sum(x[2:5]))
+
+
+def test_row_sum_matches_numpy_pairwise():
+    x = _rand(7, 4096, std=2.0)
+    np.testing.assert_allclose(oracle.row_sum(x), x.astype(np.float64).sum(axis=1), rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 1024, 4097])
+def test_row_minmax_matches_numpy_and_is_order_free(n):
+    x = _rand(7, n, seed=500 + n, std=5.0)
+    lo, hi = oracle.row_minmax(x)
+    assert np.array_equal(lo, x.min(axis=1)) and np.array_equal(hi, x.max(axis=1))
+    perm = np.random.default_rng(n).permutation(n)
+    lo2, hi2 = oracle.row_minmax(x[:, perm])
+    assert np.array_equal(lo, lo2) and np.array_equal(hi, hi2)
+    assert (lo <= hi).all()
+
+
+def test_row_minmax_extremes_at_the_ends():
+    # the extremes sit in the first and the last column: a loop that skips
+    # either end fails
+    x = np.zeros((3, 50), np.float32)
+    x[:, 0] = -7.0
+    x[:, -1] = 9.0
+    x[1, 0], x[1, -1] = 9.5, -8.0
+    lo, hi = oracle.row_minmax(x)
+    assert list(lo) == [-7.0, -8.0, -7.0] and list(hi) == [9.0, 9.5, 9.0]
+
+
+# --------------------------------------------------------------------------
 # cross-entropy
 # --------------------------------------------------------------------------
 
