@@ -277,6 +277,28 @@ def main():
             "pct_of_hbm_peak": round(100 * cb / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": cb,
             "plan": {k: v for k, v in p.as_dict().items() if k in (
                 "family", "waves_per_row", "rows_per_block", "chunks_per_lane", "threads_per_block")}}
+        # row sum and row minimum/maximum over the same logits (read-only ops)
+        rsum = torch.empty(4096, device=dev)
+        rmin, rmax = torch.empty(4096, device=dev), torch.empty(4096, device=dev)
+        for name, fn, outb in (
+            ("row_sum_4096x32000_cold",
+             lambda i: lr.lib.lr_row_sum_f32(cx[i % 2].data_ptr(), rsum.data_ptr(), 4096, 32000, 0, sh), 4),
+            ("row_minmax_4096x32000_cold",
+             lambda i: lr.lib.lr_row_minmax_f32(cx[i % 2].data_ptr(), rmin.data_ptr(), rmax.data_ptr(), 4096,
+                                                32000, 0, sh), 8)):
+            for i in range(10):
+                lr.check(fn(i), name)
+            torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(n):
+                fn(i)
+            z.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(z) * 1e3 / n
+            rb = 4096 * 32000 * 4 + 4096 * outb
+            extra[name] = {"us_per_op": round(us, 3), "gbps": round(rb / us / 1e3, 1),
+                           "pct_of_hbm_peak": round(100 * rb / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": rb}
         del cx
         out["extra"] = extra
 

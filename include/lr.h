@@ -1,11 +1,12 @@
 /*
  * lr.h -- C ABI of the MI355X (gfx950) FP32 row-reduction library, liblr.so.
  *
- * Four row operations over a row-major rows x cols FP32 tensor (row stride =
- * cols elements).  Each is a composition of max/add folds over the column
+ * Row operations over a row-major rows x cols FP32 tensor (row stride = cols
+ * elements).  Each is a composition of max/min/add folds over the column
  * axis, as defined on the page "TIRx Metal reduction lowering"
  * (LuisaCompute), section 1 (softmax and cross-entropy sources), section 5.1
- * (LayerNorm statistics), section 5.2 (guarded label gather).  The
+ * (LayerNorm statistics and the fused residual LayerNorm), section 5.2
+ * (guarded label gather), section 8 (row sums, row minimum and maximum).  The
  * reduction-order contract (unordered tree versus ordered fold) is the
  * ReductionPolicy of section 1.
  *
@@ -76,7 +77,9 @@ typedef enum lr_op {
     LR_OP_RMSNORM = 1,
     LR_OP_LAYERNORM = 2,
     LR_OP_CROSS_ENTROPY = 3,
-    LR_OP_ADD_LAYERNORM = 4
+    LR_OP_ADD_LAYERNORM = 4,
+    LR_OP_ROW_SUM = 5,
+    LR_OP_ROW_MINMAX = 6
 } lr_op;
 
 /* Kernel families.
@@ -181,6 +184,24 @@ lr_status lr_add_layernorm_f32(const float* x, const float* residual, const floa
                                int64_t cols, float eps, lr_reduction_policy policy,
                                hipStream_t stream);
 
+/* Row sum: the plain add fold over the column axis ("TIRx Metal reduction
+ * lowering", section 8 checks row sums at widths 127, 257, 1024, 4096):
+ *   sums[r] = sum_j x[r][j]   (FP32 accumulation).
+ * x: rows*cols FP32 in; sums: rows FP32 out.  Under LR_ORDERED_FOLD the sum
+ * is one FP32 chain j = 0 .. cols-1 from +0.0f; under LR_UNORDERED_TREE any
+ * order (lane stripes, then trees).  sums must not overlap x. */
+lr_status lr_row_sum_f32(const float* x, float* sums, int64_t rows, int64_t cols,
+                         lr_reduction_policy policy, hipStream_t stream);
+
+/* Row minimum and maximum together, in one pass over the row (section 8:
+ * minimum and maximum at 7 x 1024):
+ *   mins[r] = min_j x[r][j],  maxs[r] = max_j x[r][j].
+ * mins, maxs: rows FP32 out each; either may be NULL, not both
+ * (LR_ERR_NULL_POINTER).  Exact (both are input values), so every policy
+ * gives the same result.  Outputs must not overlap x or each other. */
+lr_status lr_row_minmax_f32(const float* x, float* mins, float* maxs, int64_t rows,
+                            int64_t cols, lr_reduction_policy policy, hipStream_t stream);
+
 /* The same operations under an explicit plan (the pages' exact
  * thread/packing constraints, section 6: honoured exactly or rejected).
  * `plan->family` must be LR_FAMILY_ORDERED exactly when policy is
@@ -207,6 +228,12 @@ lr_status lr_add_layernorm_f32_with_plan(const float* x, const float* residual,
                                          float* sum_out, int64_t rows, int64_t cols, float eps,
                                          lr_reduction_policy policy, const lr_plan* plan,
                                          hipStream_t stream);
+lr_status lr_row_sum_f32_with_plan(const float* x, float* sums, int64_t rows, int64_t cols,
+                                   lr_reduction_policy policy, const lr_plan* plan,
+                                   hipStream_t stream);
+lr_status lr_row_minmax_f32_with_plan(const float* x, float* mins, float* maxs, int64_t rows,
+                                      int64_t cols, lr_reduction_policy policy,
+                                      const lr_plan* plan, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Planner (host only; no device memory touched)

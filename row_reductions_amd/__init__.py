@@ -25,9 +25,11 @@ LR_ORDERED_FOLD = 1
 POLICIES = {"unordered_tree": LR_UNORDERED_TREE, "ordered_fold": LR_ORDERED_FOLD}
 
 # lr_op
-LR_OP_SOFTMAX, LR_OP_RMSNORM, LR_OP_LAYERNORM, LR_OP_CROSS_ENTROPY, LR_OP_ADD_LAYERNORM = 0, 1, 2, 3, 4
+LR_OP_SOFTMAX, LR_OP_RMSNORM, LR_OP_LAYERNORM, LR_OP_CROSS_ENTROPY = 0, 1, 2, 3
+LR_OP_ADD_LAYERNORM, LR_OP_ROW_SUM, LR_OP_ROW_MINMAX = 4, 5, 6
 OPS = {"softmax": LR_OP_SOFTMAX, "rmsnorm": LR_OP_RMSNORM, "layernorm": LR_OP_LAYERNORM,
-       "cross_entropy": LR_OP_CROSS_ENTROPY, "add_layernorm": LR_OP_ADD_LAYERNORM}
+       "cross_entropy": LR_OP_CROSS_ENTROPY, "add_layernorm": LR_OP_ADD_LAYERNORM,
+       "row_sum": LR_OP_ROW_SUM, "row_minmax": LR_OP_ROW_MINMAX}
 
 # lr_family
 LR_FAMILY_CACHE, LR_FAMILY_STREAM, LR_FAMILY_ORDERED = 0, 1, 2
@@ -104,11 +106,15 @@ def _load():
         "lr_layernorm_f32": [P, P, P, P, I64, I64, F32, I32, P],
         "lr_cross_entropy_f32": [P, P, P, I64, I64, I32, P],
         "lr_add_layernorm_f32": [P, P, P, P, P, P, I64, I64, F32, I32, P],
+        "lr_row_sum_f32": [P, P, I64, I64, I32, P],
+        "lr_row_minmax_f32": [P, P, P, I64, I64, I32, P],
         "lr_softmax_f32_with_plan": [P, P, I64, I64, I32, PP, P],
         "lr_rmsnorm_f32_with_plan": [P, P, P, I64, I64, F32, I32, PP, P],
         "lr_layernorm_f32_with_plan": [P, P, P, P, I64, I64, F32, I32, PP, P],
         "lr_cross_entropy_f32_with_plan": [P, P, P, I64, I64, I32, PP, P],
         "lr_add_layernorm_f32_with_plan": [P, P, P, P, P, P, I64, I64, F32, I32, PP, P],
+        "lr_row_sum_f32_with_plan": [P, P, I64, I64, I32, PP, P],
+        "lr_row_minmax_f32_with_plan": [P, P, P, I64, I64, I32, PP, P],
         "lr_device_facts_query": [PF],
         "lr_plan_query": [I32, I64, I64, I32, PP],
         "lr_plan_for_device": [PF, I32, I64, I64, I32, I32, PP],
@@ -207,6 +213,21 @@ def lr_add_layernorm_f32(x, residual, gamma, beta, y, sum_out, rows, cols, eps, 
     return lib.lr_add_layernorm_f32_with_plan(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y),
                                               _ptr(sum_out), rows, cols, eps, _policy(policy),
                                               ctypes.byref(plan), _stream(stream))
+
+
+def lr_row_sum_f32(x, sums, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None) -> int:
+    if plan is None:
+        return lib.lr_row_sum_f32(_ptr(x), _ptr(sums), rows, cols, _policy(policy), _stream(stream))
+    return lib.lr_row_sum_f32_with_plan(_ptr(x), _ptr(sums), rows, cols, _policy(policy), ctypes.byref(plan),
+                                        _stream(stream))
+
+
+def lr_row_minmax_f32(x, mins, maxs, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None) -> int:
+    if plan is None:
+        return lib.lr_row_minmax_f32(_ptr(x), _ptr(mins), _ptr(maxs), rows, cols, _policy(policy),
+                                     _stream(stream))
+    return lib.lr_row_minmax_f32_with_plan(_ptr(x), _ptr(mins), _ptr(maxs), rows, cols, _policy(policy),
+                                           ctypes.byref(plan), _stream(stream))
 
 
 def lr_device_facts_mi355x() -> LrDeviceFacts:

@@ -42,6 +42,8 @@ SOURCES = [
     "k_layernorm.hip",
     "k_cross_entropy.hip",
     "k_add_layernorm.hip",
+    "k_row_sum.hip",
+    "k_row_minmax.hip",
     "k_ordered.hip",
 ]
 

@@ -100,6 +100,22 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
             float* yr = a.y + row * (int64_t)cols;
             for (int e = lane; e < cols; e += kWave) yr[e] = expf(xr[e] - m) / s;
         }
+    } else if constexpr (OP == kRowSum) {
+        const float sum = ordered_fold<kValue>(xr, nullptr, cols, 0.0f, slab, lane);
+        if (lane == 0) a.sums[row] = sum;
+    } else if constexpr (OP == kRowMinMax) {
+        // exact in any order: the wave tree, as the max fold above
+        float lo = INFINITY, hi = -INFINITY;
+        for (int e = lane; e < cols; e += kWave) {
+            lo = fmin2(lo, xr[e]);
+            hi = fmax2(hi, xr[e]);
+        }
+        lo = wave_allreduce<MinOp>(lo);
+        hi = wave_allreduce<MaxOp>(hi);
+        if (lane == 0) {
+            if (a.mins) a.mins[row] = lo;
+            if (a.maxs) a.maxs[row] = hi;
+        }
     } else if constexpr (OP == kRmsNorm) {
         const float ss = ordered_fold<kSquare>(xr, nullptr, cols, 0.0f, slab, lane);
         const float ms = ss / n;
@@ -137,6 +153,8 @@ hipError_t launch_ordered(int op, const KArgs& a, const lr_plan& p, hipStream_t 
         case kLayerNorm: hipLaunchKernelGGL(k_ordered<kLayerNorm>, grid, block, 0, s, a); break;
         case kCrossEntropy: hipLaunchKernelGGL(k_ordered<kCrossEntropy>, grid, block, 0, s, a); break;
         case kAddLayerNorm: hipLaunchKernelGGL(k_ordered<kAddLayerNorm>, grid, block, 0, s, a); break;
+        case kRowSum: hipLaunchKernelGGL(k_ordered<kRowSum>, grid, block, 0, s, a); break;
+        case kRowMinMax: hipLaunchKernelGGL(k_ordered<kRowMinMax>, grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -71,14 +71,21 @@ struct Call {
     int policy;
     const float* residual = nullptr;  // fused residual LayerNorm
     float* sum_out = nullptr;         // fused residual LayerNorm, optional
+    float* sums = nullptr;            // row sum
+    float* mins = nullptr;            // row minimum, optional
+    float* maxs = nullptr;            // row maximum, optional
 };
 
 lr_status validate_call(const Call& c) {
     if (c.policy != LR_UNORDERED_TREE && c.policy != LR_ORDERED_FOLD) return LR_ERR_INVALID_POLICY;
     const bool ce = c.op == LR_OP_CROSS_ENTROPY;
     const bool res = c.op == LR_OP_ADD_LAYERNORM;
+    const bool per_row = ce || c.op == LR_OP_ROW_SUM || c.op == LR_OP_ROW_MINMAX;  // one value per row out
     if (c.x == nullptr) return LR_ERR_NULL_POINTER;
-    if (ce ? (c.labels == nullptr || c.losses == nullptr) : c.y == nullptr) return LR_ERR_NULL_POINTER;
+    if (ce && (c.labels == nullptr || c.losses == nullptr)) return LR_ERR_NULL_POINTER;
+    if (c.op == LR_OP_ROW_SUM && c.sums == nullptr) return LR_ERR_NULL_POINTER;
+    if (c.op == LR_OP_ROW_MINMAX && c.mins == nullptr && c.maxs == nullptr) return LR_ERR_NULL_POINTER;
+    if (!per_row && c.y == nullptr) return LR_ERR_NULL_POINTER;
     if (res && c.residual == nullptr) return LR_ERR_NULL_POINTER;
     if (c.rows < 0 || c.cols < 1 || c.cols >= (int64_t(1) << 24) || c.rows > INT32_MAX) return LR_ERR_INVALID_SHAPE;
     if (c.rows > INT64_MAX / 4 / c.cols) return LR_ERR_INVALID_SHAPE;
@@ -87,7 +94,7 @@ lr_status validate_call(const Call& c) {
     }
     auto a4 = [](const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!a4(c.x) || !a4(c.y) || !a4(c.gamma) || !a4(c.beta) || !a4(c.losses) || !a4(c.residual) ||
-        !a4(c.sum_out))
+        !a4(c.sum_out) || !a4(c.sums) || !a4(c.mins) || !a4(c.maxs))
         return LR_ERR_MISALIGNED;
     if (c.labels != nullptr && (reinterpret_cast<uintptr_t>(c.labels) & 7u) != 0) return LR_ERR_MISALIGNED;
     const int64_t tb = c.rows * c.cols * 4;
@@ -95,6 +102,15 @@ lr_status validate_call(const Call& c) {
     if (ce) {
         const Range rl = range_of(c.losses, c.rows * 4), rlab = range_of(c.labels, c.rows * 8);
         if (c.rows > 0 && (overlap(rl, rx) || overlap(rl, rlab))) return LR_ERR_ALIASING;
+    } else if (per_row) {
+        const float* outs[3] = {c.sums, c.mins, c.maxs};
+        for (int i = 0; i < 3 && c.rows > 0; ++i) {
+            if (outs[i] == nullptr) continue;
+            const Range ro = range_of(outs[i], c.rows * 4);
+            if (overlap(ro, rx)) return LR_ERR_ALIASING;
+            for (int j = i + 1; j < 3; ++j)
+                if (outs[j] != nullptr && overlap(ro, range_of(outs[j], c.rows * 4))) return LR_ERR_ALIASING;
+        }
     } else if (c.rows > 0) {
         // an output may be exactly one of the row inputs (in place); any other
         // overlap with an input, or between the two outputs, is rejected
@@ -121,9 +137,10 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     if (st != LR_OK) return st;
     if (c.rows == 0) return LR_OK;  // nothing to launch
     const bool ce = c.op == LR_OP_CROSS_ENTROPY;
+    const bool per_row = ce || c.op == LR_OP_ROW_SUM || c.op == LR_OP_ROW_MINMAX;
     const bool rows_aligned = c.cols % kVec == 0 && aligned16(c.x);
-    const bool aligned = rows_aligned && (ce || (aligned16(c.y) && aligned16(c.gamma) && aligned16(c.beta) &&
-                                                 aligned16(c.residual) && aligned16(c.sum_out)));
+    const bool aligned = rows_aligned && (per_row || (aligned16(c.y) && aligned16(c.gamma) && aligned16(c.beta) &&
+                                                      aligned16(c.residual) && aligned16(c.sum_out)));
 
     lr_device_facts facts;
     st = current_facts(&facts);
@@ -158,7 +175,10 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
                             : (int32_t)((reinterpret_cast<uintptr_t>(p) & 15u) ==
                                         (reinterpret_cast<uintptr_t>(c.x) & 15u));
     };
-    a.y_same_phase = ce ? 1 : same_phase(c.y);
+    a.y_same_phase = per_row ? 1 : same_phase(c.y);
+    a.sums = c.sums;
+    a.mins = c.mins;
+    a.maxs = c.maxs;
     a.residual = c.residual;
     a.sum_out = c.sum_out;
     a.r_same_phase = same_phase(c.residual);
@@ -174,6 +194,8 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
             case LR_OP_RMSNORM: e = launch_rmsnorm(a, plan, aligned, stream); break;
             case LR_OP_LAYERNORM: e = launch_layernorm(a, plan, aligned, stream); break;
             case LR_OP_ADD_LAYERNORM: e = launch_add_layernorm(a, plan, aligned, stream); break;
+            case LR_OP_ROW_SUM: e = launch_row_sum(a, plan, aligned, stream); break;
+            case LR_OP_ROW_MINMAX: e = launch_row_minmax(a, plan, aligned, stream); break;
             default: e = launch_cross_entropy(a, plan, aligned, stream); break;
         }
     }
@@ -221,6 +243,21 @@ lr_status lr_add_layernorm_f32(const float* x, const float* residual, const floa
     return lr::run(c, nullptr, stream);
 }
 
+lr_status lr_row_sum_f32(const float* x, float* sums, int64_t rows, int64_t cols, lr_reduction_policy policy,
+                         hipStream_t stream) {
+    Call c{LR_OP_ROW_SUM, x, nullptr, nullptr, nullptr, nullptr, nullptr, rows, cols, 0.0f, policy};
+    c.sums = sums;
+    return lr::run(c, nullptr, stream);
+}
+
+lr_status lr_row_minmax_f32(const float* x, float* mins, float* maxs, int64_t rows, int64_t cols,
+                            lr_reduction_policy policy, hipStream_t stream) {
+    Call c{LR_OP_ROW_MINMAX, x, nullptr, nullptr, nullptr, nullptr, nullptr, rows, cols, 0.0f, policy};
+    c.mins = mins;
+    c.maxs = maxs;
+    return lr::run(c, nullptr, stream);
+}
+
 static lr_status need_plan(const lr_plan* plan) { return plan == nullptr ? LR_ERR_NULL_POINTER : LR_OK; }
 
 lr_status lr_softmax_f32_with_plan(const float* x, float* y, int64_t rows, int64_t cols,
@@ -263,6 +300,23 @@ lr_status lr_add_layernorm_f32_with_plan(const float* x, const float* residual, 
     Call c{LR_OP_ADD_LAYERNORM, x, gamma, beta, y, nullptr, nullptr, rows, cols, eps, policy};
     c.residual = residual;
     c.sum_out = sum_out;
+    return lr::run(c, plan, stream);
+}
+
+lr_status lr_row_sum_f32_with_plan(const float* x, float* sums, int64_t rows, int64_t cols,
+                                   lr_reduction_policy policy, const lr_plan* plan, hipStream_t stream) {
+    if (need_plan(plan) != LR_OK) return LR_ERR_NULL_POINTER;
+    Call c{LR_OP_ROW_SUM, x, nullptr, nullptr, nullptr, nullptr, nullptr, rows, cols, 0.0f, policy};
+    c.sums = sums;
+    return lr::run(c, plan, stream);
+}
+
+lr_status lr_row_minmax_f32_with_plan(const float* x, float* mins, float* maxs, int64_t rows, int64_t cols,
+                                      lr_reduction_policy policy, const lr_plan* plan, hipStream_t stream) {
+    if (need_plan(plan) != LR_OK) return LR_ERR_NULL_POINTER;
+    Call c{LR_OP_ROW_MINMAX, x, nullptr, nullptr, nullptr, nullptr, nullptr, rows, cols, 0.0f, policy};
+    c.mins = mins;
+    c.maxs = maxs;
     return lr::run(c, plan, stream);
 }
 

@@ -9,7 +9,15 @@
 
 namespace lr {
 
-enum Op : int { kSoftmax = 0, kRmsNorm = 1, kLayerNorm = 2, kCrossEntropy = 3, kAddLayerNorm = 4 };
+enum Op : int {
+    kSoftmax = 0,
+    kRmsNorm = 1,
+    kLayerNorm = 2,
+    kCrossEntropy = 3,
+    kAddLayerNorm = 4,
+    kRowSum = 5,
+    kRowMinMax = 6
+};
 
 // LayerNorm statistics (mean, then centred variance) with a per-column affine.
 constexpr bool is_layernorm(int op) { return op == kLayerNorm || op == kAddLayerNorm; }
@@ -41,9 +49,15 @@ struct AddOp {
 // operands per instruction.
 __device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+__device__ __forceinline__ float fmin2(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
 struct MaxOp {
     static __device__ __forceinline__ float apply(float a, float b) { return fmax2(a, b); }
     static constexpr float identity() { return -INFINITY; }
+};
+struct MinOp {
+    static __device__ __forceinline__ float apply(float a, float b) { return fmin2(a, b); }
+    static constexpr float identity() { return INFINITY; }
 };
 
 template <class R>

@@ -29,6 +29,9 @@ struct KArgs {
     float* sum_out;         // fused residual LayerNorm: x + residual out, or null
     int32_t r_same_phase;   // residual rows start at the same 16-byte phase as x rows
     int32_t s_same_phase;   // sum_out rows start at the same 16-byte phase as x rows
+    float* sums;            // row sum: one float per row
+    float* mins;            // row minimum (or null)
+    float* maxs;            // row maximum (or null)
 };
 
 // Compiled cache-family chunk counts (chunks_per_lane), ascending.
@@ -49,6 +52,8 @@ hipError_t launch_rmsnorm(const KArgs& a, const lr_plan& p, bool aligned, hipStr
 hipError_t launch_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_cross_entropy(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_add_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_row_sum(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_row_minmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_ordered(int op, const KArgs& a, const lr_plan& p, hipStream_t s);
 
 }  // namespace lr

@@ -20,7 +20,27 @@ namespace lr {
 
 template <int OP>
 constexpr float op_identity() {
-    return (OP == kSoftmax || OP == kCrossEntropy) ? -INFINITY : 0.0f;
+    // row minimum and maximum share one stripe: missing elements hold NaN,
+    // which the minimum/maximum-number folds skip
+    return (OP == kSoftmax || OP == kCrossEntropy) ? -INFINITY : (OP == kRowMinMax ? __builtin_nanf("") : 0.0f);
+}
+
+// IEEE minNum / maxNum: a NaN operand yields the other one.
+__device__ __forceinline__ float fminnum(float a, float b) { return __builtin_fminf(a, b); }
+__device__ __forceinline__ float fmaxnum(float a, float b) { return __builtin_fmaxf(a, b); }
+
+// Writes the row's minimum and maximum after the stripe folds: a lane that
+// held no element of the row still has NaN and takes the identities.
+__device__ __forceinline__ void finish_minmax(const KArgs& a, float lo, float hi, float* red_lo, float* red_hi,
+                                              int S, const Team& t, bool active, int64_t row) {
+    lo = __builtin_isnan(lo) ? INFINITY : lo;
+    hi = __builtin_isnan(hi) ? -INFINITY : hi;
+    lo = team_reduce<MinOp>(lo, red_lo, S, t);
+    hi = team_reduce<MaxOp>(hi, red_hi, S, t);
+    if (active && t.w == 0) {
+        if (a.mins) a.mins[row] = lo;
+        if (a.maxs) a.maxs[row] = hi;
+    }
 }
 
 // Reads label[row] and the guarded logit once per row (worker 0 of the team).
@@ -206,6 +226,20 @@ k_cache(const KArgs a) {
                 }
             }
         }
+    } else if constexpr (OP == kRowSum) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) sum += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+        sum = team_reduce<AddOp>(sum, red[0], S, t);
+        if (active && t.w == 0) a.sums[row] = sum;
+    } else if constexpr (OP == kRowMinMax) {
+        float lo = ID, hi = ID;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            lo = fminnum(fminnum(lo, fminnum(v[c].x, v[c].y)), fminnum(v[c].z, v[c].w));
+            hi = fmaxnum(fmaxnum(hi, fmaxnum(v[c].x, v[c].y)), fmaxnum(v[c].z, v[c].w));
+        }
+        finish_minmax(a, lo, hi, red[0], red[1], S, t, active, row);
     } else if constexpr (OP == kRmsNorm) {
         float ss = 0.0f;
 #pragma unroll
@@ -350,6 +384,28 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
                 }
             }
         }
+    } else if constexpr (OP == kRowSum) {
+        float sum = 0.0f;
+        for (int k0 = t.w; k0 < nv; k0 += W * U) {
+            float4 v[U];
+            load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
+#pragma unroll
+            for (int u = 0; u < U; ++u) sum += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+        }
+        sum = team_reduce<AddOp>(sum, red[0], S, t);
+        if (active && t.w == 0) a.sums[row] = sum;
+    } else if constexpr (OP == kRowMinMax) {
+        float lo = ID, hi = ID;
+        for (int k0 = t.w; k0 < nv; k0 += W * U) {
+            float4 v[U];
+            load_trip<OP, AL>(v, xa, rr, k0, W, nv, h, cols, ID);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                lo = fminnum(fminnum(lo, fminnum(v[u].x, v[u].y)), fminnum(v[u].z, v[u].w));
+                hi = fmaxnum(fmaxnum(hi, fmaxnum(v[u].x, v[u].y)), fmaxnum(v[u].z, v[u].w));
+            }
+        }
+        finish_minmax(a, lo, hi, red[0], red[1], S, t, active, row);
     } else if constexpr (OP == kRmsNorm) {
         float ss = 0.0f;
         for (int k0 = t.w; k0 < nv; k0 += W * U) {
@@ -451,7 +507,7 @@ hipError_t launch_cache_nch(const KArgs& a, const lr_plan& p, hipStream_t s) {
 // Selects the parameter mode from which parameters are present.
 template <int OP, bool AL>
 hipError_t launch_cache_pm(const KArgs& a, const lr_plan& p, hipStream_t s) {
-    if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
+    if constexpr (num_params<OP>() == 0) {
         return launch_cache_nch<OP, AL, kParNone>(a, p, s);
     } else {
         const bool all = a.gamma != nullptr && (OP == kRmsNorm || a.beta != nullptr);

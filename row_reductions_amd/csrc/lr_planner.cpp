@@ -31,7 +31,7 @@ static int64_t max_row_chunks(int64_t cols, bool aligned) {
 }
 
 static int reductions_of(int op) {
-    return op == LR_OP_RMSNORM ? 1 : 2;
+    return (op == LR_OP_RMSNORM || op == LR_OP_ROW_SUM) ? 1 : 2;
 }
 
 static int smallest_cache_instance(int64_t need) {
@@ -56,7 +56,7 @@ static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_
     return p;
 }
 
-static bool valid_op(int op) { return op >= LR_OP_SOFTMAX && op <= LR_OP_ADD_LAYERNORM; }
+static bool valid_op(int op) { return op >= LR_OP_SOFTMAX && op <= LR_OP_ROW_MINMAX; }
 static bool valid_policy(int p) { return p == LR_UNORDERED_TREE || p == LR_ORDERED_FOLD; }
 
 static lr_status check_problem(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy) {

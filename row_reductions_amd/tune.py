@@ -24,7 +24,7 @@ import torch
 import row_reductions_amd as lr
 
 
-def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh, rs=None):
+def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh, rs=None, ys2=None):
     pol = lr._policy(policy)
 
     def run(i, plan):
@@ -37,6 +37,10 @@ def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh, rs=None):
             return lr.lr_layernorm_f32(xs[k], g, b, ys[k], rows, cols, eps, pol, sh, plan)
         if op == "add_layernorm":
             return lr.lr_add_layernorm_f32(xs[k], rs[k], g, b, ys[k], None, rows, cols, eps, pol, sh, plan)
+        if op == "row_sum":
+            return lr.lr_row_sum_f32(xs[k], ys[k], rows, cols, pol, sh, plan)
+        if op == "row_minmax":
+            return lr.lr_row_minmax_f32(xs[k], ys[k], ys2[k], rows, cols, pol, sh, plan)
         return lr.lr_cross_entropy_f32(xs[k], lab, ys[k], rows, cols, pol, sh, plan)
     return run
 
@@ -76,8 +80,12 @@ def main(argv=None):
     sets = args.sets or max(2, min(64, -(-(1 << 30) // (2 * tensor_bytes))))
     gen = torch.Generator(device=dev).manual_seed(0)
     x0 = torch.randn(rows, cols, device=dev, generator=gen)
+    if op == "row_sum":
+        x0 = x0.abs()  # positive rows: sums of any order agree to the relative bar
     xs = [x0] + [x0.clone() for _ in range(sets - 1)]
-    if op == "cross_entropy":
+    per_row = op in ("cross_entropy", "row_sum", "row_minmax")
+    ys2 = [torch.empty(rows, device=dev) for _ in range(sets)] if op == "row_minmax" else None
+    if per_row:
         ys = [torch.empty(rows, device=dev) for _ in range(sets)]
     else:
         ys = [torch.empty_like(x0) for _ in range(sets)]
@@ -85,7 +93,7 @@ def main(argv=None):
     b = torch.randn(cols, device=dev, generator=gen) * 0.1
     lab = torch.randint(0, cols, (rows,), device=dev, generator=gen)
     rs = [torch.randn(rows, cols, device=dev, generator=gen) for _ in range(sets)] if op == "add_layernorm" else None
-    run = _launcher(op, xs, ys, g, b, lab, rows, cols, args.eps, args.policy, sh, rs)
+    run = _launcher(op, xs, ys, g, b, lab, rows, cols, args.eps, args.policy, sh, rs, ys2)
 
     facts = lr.lr_device_facts_query()
     aligned = 1 if cols % 4 == 0 else 0
@@ -110,7 +118,8 @@ def main(argv=None):
     results.sort(key=lambda t: t[0])
     best_us, best, _ = results[0]
     again = _time(run, best, args.iters, stream)
-    moved = {"cross_entropy": tensor_bytes + rows * 12, "add_layernorm": 3 * tensor_bytes}.get(op, 2 * tensor_bytes)
+    moved = {"cross_entropy": tensor_bytes + rows * 12, "add_layernorm": 3 * tensor_bytes,
+             "row_sum": tensor_bytes + rows * 4, "row_minmax": tensor_bytes + rows * 8}.get(op, 2 * tensor_bytes)
     print(f"# {op} {rows}x{cols} {args.policy}: {len(results)} candidates, "
           f"automatic {_time(run, auto, args.iters, stream):.2f} us, "
           f"best {again:.2f} us ({moved / again / 1e3:.0f} GB/s): {best!r}")
@@ -118,7 +127,7 @@ def main(argv=None):
         print(f"#   {us:8.2f} us  {p!r}")
     fam = {0: "LR_FAMILY_CACHE", 1: "LR_FAMILY_STREAM", 2: "LR_FAMILY_ORDERED"}[best.family]
     opn = {0: "LR_OP_SOFTMAX", 1: "LR_OP_RMSNORM", 2: "LR_OP_LAYERNORM", 3: "LR_OP_CROSS_ENTROPY",
-           4: "LR_OP_ADD_LAYERNORM"}[lr.OPS[op]]
+           4: "LR_OP_ADD_LAYERNORM", 5: "LR_OP_ROW_SUM", 6: "LR_OP_ROW_MINMAX"}[lr.OPS[op]]
     pol = "LR_ORDERED_FOLD" if args.policy == "ordered_fold" else "LR_UNORDERED_TREE"
     print(f"{{{opn}, {pol}, {rows}, {cols}, {aligned}, {fam}, {best.waves_per_row}, "
           f"{best.rows_per_block}, {best.chunks_per_lane}}},")

@@ -45,6 +45,8 @@ def test_zero_rows_is_ok_without_launch():
     assert lr.lr_layernorm_f32(X, None, None, Y, 0, 7, 1e-5, 0, 0) == lr.LR_OK
     assert lr.lr_cross_entropy_f32(X, LAB, LOSS, 0, 32000, 0, 0) == lr.LR_OK
     assert lr.lr_add_layernorm_f32(X, RES, None, None, Y, SUM, 0, 7, 1e-5, 0, 0) == lr.LR_OK
+    assert lr.lr_row_sum_f32(X, LOSS, 0, 7, 1, 0) == lr.LR_OK
+    assert lr.lr_row_minmax_f32(X, LOSS, None, 0, 7, 0, 0) == lr.LR_OK
 
 
 @pytest.mark.parametrize("call,status", [
@@ -84,6 +86,16 @@ def test_zero_rows_is_ok_without_launch():
     (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, X, X, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
     (lambda: lr.lr_add_layernorm_f32(X, RES, Y + 8, B, Y, SUM, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
     (lambda: lr.lr_add_layernorm_f32(X, RES, G, SUM + 8, Y, SUM, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
+    # row sum, row minimum and maximum
+    (lambda: lr.lr_row_sum_f32(X, None, 4, 8, 0, 0), lr.LR_ERR_NULL_POINTER),
+    (lambda: lr.lr_row_minmax_f32(X, None, None, 4, 8, 0, 0), lr.LR_ERR_NULL_POINTER),
+    (lambda: lr.lr_row_sum_f32(X, LOSS + 2, 4, 8, 0, 0), lr.LR_ERR_MISALIGNED),
+    (lambda: lr.lr_row_minmax_f32(X, None, LOSS + 1, 4, 8, 0, 0), lr.LR_ERR_MISALIGNED),
+    (lambda: lr.lr_row_sum_f32(X, LOSS, 4, 8, 5, 0), lr.LR_ERR_INVALID_POLICY),
+    (lambda: lr.lr_row_sum_f32(X, X + 64, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_row_minmax_f32(X, LOSS, LOSS + 8, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_row_minmax_f32(X, LOSS, LOSS, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
+    (lambda: lr.lr_row_minmax_f32(X, X, None, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
     # y is x in place, but x and the residual overlap partially: rows would race
     (lambda: lr.lr_add_layernorm_f32(X, X + 16, G, B, X, None, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
 ])
@@ -106,3 +118,5 @@ def test_valid_call_without_device_reports_hip_error():
     assert lr.lr_add_layernorm_f32(X, RES, G, B, X, RES, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP
     assert lr.lr_add_layernorm_f32(X, RES, None, None, RES, X, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP
     assert lr.lr_add_layernorm_f32(X, X, None, None, Y, None, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP
+    assert lr.lr_row_sum_f32(X, LOSS, 4, 8, 1, 0) == lr.LR_ERR_HIP
+    assert lr.lr_row_minmax_f32(X, None, LOSS, 4, 8, 0, 0) == lr.LR_ERR_HIP

@@ -11,7 +11,7 @@ import pytest
 import row_reductions_amd as lr
 
 F = lr.lr_device_facts_mi355x()
-OPS = ["softmax", "rmsnorm", "layernorm", "cross_entropy", "add_layernorm"]
+OPS = ["softmax", "rmsnorm", "layernorm", "cross_entropy", "add_layernorm", "row_sum", "row_minmax"]
 
 WIDTHS = list(range(1, 131)) + [255, 256, 257, 511, 513, 1023, 1024, 1025, 1537, 3072, 6144, 12289]
 
