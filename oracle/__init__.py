@@ -59,6 +59,12 @@ def _load():
         lib.oracle_layernorm_fold_f32.argtypes = [P, P, P, P, I64, I64, ctypes.c_float]
         lib.oracle_fold_left_f32.argtypes = [P, I64, ctypes.c_int]
         lib.oracle_fold_left_f32.restype = ctypes.c_float
+        lib.oracle_ordered_sum_f32.argtypes = [P, I64, ctypes.c_int, ctypes.c_int]
+        lib.oracle_ordered_sum_f32.restype = ctypes.c_float
+        lib.oracle_rmsnorm_ordered_f32.argtypes = [P, P, P, I64, I64, ctypes.c_float, ctypes.c_int]
+        lib.oracle_rmsnorm_ordered_f32.restype = None
+        lib.oracle_layernorm_ordered_f32.argtypes = [P, P, P, P, I64, I64, ctypes.c_float, ctypes.c_int]
+        lib.oracle_layernorm_ordered_f32.restype = ctypes.c_int
         for f in ("oracle_softmax_f64", "oracle_rmsnorm_f64", "oracle_layernorm_f64",
                   "oracle_layernorm_stats_f64", "oracle_cross_entropy_f64",
                   "oracle_rmsnorm_fold_f32", "oracle_layernorm_fold_f32"):
@@ -191,6 +197,38 @@ def fold_left_f32(x, kind: int = 0) -> float:
     """FP32 left fold of a 1-D array: kind 0 sums x_j, kind 1 sums x_j*x_j."""
     a = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
     return float(_load().oracle_fold_left_f32(_ptr(a), a.shape[0], kind))
+
+
+#: the ordered reduction policies and their codes in the replay functions
+ORDERED_POLICIES = {"ordered_fold": 1, "ordered_tree": 2, "fold_right": 3}
+
+
+def ordered_sum_f32(x, policy: str, kind: int = 0) -> float:
+    """FP32 sum of a 1-D array in the order of an ordered policy: kind 0
+    sums x_j, kind 1 sums x_j*x_j."""
+    a = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    return float(_load().oracle_ordered_sum_f32(_ptr(a), a.shape[0], kind, ORDERED_POLICIES[policy]))
+
+
+def rmsnorm_ordered_f32(x, gamma=None, eps: float = 1e-6, policy: str = "ordered_fold") -> np.ndarray:
+    x = _f32(x)
+    g = _opt_vec(gamma, x.shape[1])
+    y = np.empty(x.shape, dtype=np.float32)
+    _load().oracle_rmsnorm_ordered_f32(_ptr(x), _ptr(g), _ptr(y), x.shape[0], x.shape[1], ctypes.c_float(eps),
+                                       ORDERED_POLICIES[policy])
+    return y
+
+
+def layernorm_ordered_f32(x, gamma=None, beta=None, eps: float = 1e-5, policy: str = "ordered_fold") -> np.ndarray:
+    x = _f32(x)
+    g = _opt_vec(gamma, x.shape[1])
+    b = _opt_vec(beta, x.shape[1])
+    y = np.empty(x.shape, dtype=np.float32)
+    rc = _load().oracle_layernorm_ordered_f32(_ptr(x), _ptr(g), _ptr(b), _ptr(y), x.shape[0], x.shape[1],
+                                              ctypes.c_float(eps), ORDERED_POLICIES[policy])
+    if rc != 0:
+        raise MemoryError("oracle_layernorm_ordered_f32: row scratch")
+    return y
 
 
 def run(op: str, inputs: dict, eps=None) -> np.ndarray:

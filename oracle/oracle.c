@@ -178,6 +178,87 @@ float oracle_fold_left_f32(const float* x, int64_t n, int kind) {
     return acc;
 }
 
+/* fold_right: the same chain taken from the right end, acc = c_j + acc for
+ * j = n-1, n-2, ..., 0, starting from +0.0f. */
+float oracle_fold_right_f32(const float* x, int64_t n, int kind) {
+    float acc = 0.0f;
+    for (int64_t j = n - 1; j >= 0; --j) {
+        float c = (kind == 1) ? x[j] * x[j] : x[j];
+        acc = c + acc;
+    }
+    return acc;
+}
+
+/* ordered_tree (reading used: the pairwise tree in index order).  The row's
+ * contributions c_0 .. c_{n-1} are padded with the add identity +0.0f to the
+ * next power of two; each level adds adjacent pairs, node 2i + node 2i+1,
+ * until one value is left.  Every addition is one FP32 rounding. */
+float oracle_tree_f32(const float* x, int64_t n, int kind) {
+    int64_t p = 1;
+    while (p < n) p *= 2;
+    float* t = (float*)malloc((size_t)p * sizeof(float));
+    if (t == NULL) return NAN;
+    for (int64_t j = 0; j < p; ++j) {
+        float c = 0.0f;
+        if (j < n) c = (kind == 1) ? x[j] * x[j] : x[j];
+        t[j] = c;
+    }
+    for (int64_t w = p; w > 1; w /= 2) {
+        for (int64_t i = 0; i < w / 2; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+    }
+    float out = t[0];
+    free(t);
+    return out;
+}
+
+/* The FP32 sum of one row's contributions in the order of `policy`:
+ * 1 fold_left, 2 ordered_tree, 3 fold_right (kind as above). */
+float oracle_ordered_sum_f32(const float* x, int64_t n, int kind, int policy) {
+    if (policy == 2) return oracle_tree_f32(x, n, kind);
+    if (policy == 3) return oracle_fold_right_f32(x, n, kind);
+    return oracle_fold_left_f32(x, n, kind);
+}
+
+/* RMSNorm and LayerNorm replays under any ordered policy: the same FP32
+ * operation sequence as the fold_left replays below, with each add
+ * reduction taken in the policy's order. */
+void oracle_rmsnorm_ordered_f32(const float* x, const float* gamma, float* y, int64_t rows,
+                                int64_t cols, float eps, int policy) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        float* yr = y + r * cols;
+        float acc = oracle_ordered_sum_f32(xr, cols, 1, policy);
+        float ms = acc / (float)cols;
+        float rr = 1.0f / sqrtf(ms + eps);
+        for (int64_t j = 0; j < cols; ++j) {
+            float t = xr[j] * rr;
+            yr[j] = gamma ? t * gamma[j] : t;
+        }
+    }
+}
+
+int oracle_layernorm_ordered_f32(const float* x, const float* gamma, const float* beta, float* y,
+                                 int64_t rows, int64_t cols, float eps, int policy) {
+    float* d = (float*)malloc((size_t)cols * sizeof(float));
+    if (d == NULL) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * cols;
+        float* yr = y + r * cols;
+        float mu = oracle_ordered_sum_f32(xr, cols, 0, policy) / (float)cols;
+        for (int64_t j = 0; j < cols; ++j) d[j] = xr[j] - mu;
+        float var = oracle_ordered_sum_f32(d, cols, 1, policy) / (float)cols;
+        float rr = 1.0f / sqrtf(var + eps);
+        for (int64_t j = 0; j < cols; ++j) {
+            float t = d[j] * rr;
+            if (gamma) t = t * gamma[j];
+            if (beta) t = t + beta[j];
+            yr[j] = t;
+        }
+    }
+    free(d);
+    return 0;
+}
+
 void oracle_rmsnorm_fold_f32(const float* x, const float* gamma, float* y,
                              int64_t rows, int64_t cols, float eps) {
     for (int64_t r = 0; r < rows; ++r) {

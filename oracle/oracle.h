@@ -78,6 +78,21 @@ void oracle_layernorm_fold_f32(const float* x, const float* gamma,
  * x_j*x_j (kind 1).  Exposed so tests can pin the fold order directly. */
 float oracle_fold_left_f32(const float* x, int64_t n, int kind);
 
+/* The other ordered policies of section 1 ("fold_right", "ordered_tree"):
+ * fold_right takes the chain from the right end (acc = c_j + acc,
+ * j = n-1 .. 0, from +0.0f).  ordered_tree (reading: the pairwise tree in
+ * index order) pads the contributions with +0.0f to the next power of two
+ * and adds adjacent pairs level by level.  Both round every operation. */
+float oracle_fold_right_f32(const float* x, int64_t n, int kind);
+float oracle_tree_f32(const float* x, int64_t n, int kind);
+/* policy: 1 fold_left, 2 ordered_tree, 3 fold_right. */
+float oracle_ordered_sum_f32(const float* x, int64_t n, int kind, int policy);
+void oracle_rmsnorm_ordered_f32(const float* x, const float* gamma, float* y, int64_t rows,
+                                int64_t cols, float eps, int policy);
+/* Returns 0, or -1 when the row scratch cannot be allocated. */
+int oracle_layernorm_ordered_f32(const float* x, const float* gamma, const float* beta, float* y,
+                                 int64_t rows, int64_t cols, float eps, int policy);
+
 #ifdef __cplusplus
 }
 #endif

@@ -480,6 +480,97 @@ def test_fold_replay_within_serial_error_of_double_oracle(op):
     assert err.max() > 0  # the replay really is FP32
 
 
+ORDERED = ["ordered_fold", "ordered_tree", "fold_right"]
+GOLDEN_ORDERED = os.path.join(os.path.dirname(__file__), "golden", "ordered_sums.json")
+
+
+def _ordered_cases():
+    with open(GOLDEN_ORDERED) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _ordered_cases(), ids=lambda c: str(c["x"]))
+def test_ordered_sums_golden(case):
+    x = np.array(case["x"], dtype=np.float32)
+    for pol, key in (("ordered_fold", "fold_left"), ("ordered_tree", "ordered_tree"), ("fold_right", "fold_right")):
+        assert oracle.ordered_sum_f32(x, pol, case["kind"]) == case[key], (pol, case)
+
+
+def test_fold_right_is_fold_left_of_the_reversed_row():
+    for n in (1, 2, 7, 1000, 4097):
+        x = _rand(1, n, seed=600 + n, mean=1.0, std=5.0)[0]
+        for kind in (0, 1):
+            a = oracle.ordered_sum_f32(x, "fold_right", kind)
+            b = oracle.ordered_sum_f32(x[::-1].copy(), "ordered_fold", kind)
+            assert np.float32(a).view(np.uint32) == np.float32(b).view(np.uint32)
+
+
+def test_tree_zero_padding_and_halves():
+    rng = np.random.default_rng(12)
+    for n in (1, 3, 5, 100, 257, 1000):
+        x = rng.normal(size=n).astype(np.float32)
+        p = 1
+        while p < n:
+            p *= 2
+        # padding with +0 up to the tree's own width, or beyond, changes nothing
+        for extra in (p - n, 2 * p - n, 4 * p - n):
+            xp = np.concatenate([x, np.zeros(extra, np.float32)])
+            assert oracle.ordered_sum_f32(xp, "ordered_tree") == oracle.ordered_sum_f32(x, "ordered_tree")
+    # a full tree is the rounded sum of its two half trees
+    for k in range(1, 12):
+        x = rng.normal(size=2 ** k).astype(np.float32)
+        h = 2 ** (k - 1)
+        whole = oracle.ordered_sum_f32(x, "ordered_tree")
+        halves = np.float32(np.float32(oracle.ordered_sum_f32(x[:h], "ordered_tree")) +
+                            np.float32(oracle.ordered_sum_f32(x[h:], "ordered_tree")))
+        assert np.float32(whole) == halves
+
+
+def test_tree_leaf_pairs_commute_but_left_fold_does_not():
+    rng = np.random.default_rng(13)
+    # magnitudes spread over twelve decades, so that every reordering is visible in a serial chain
+    x = (rng.normal(size=4096) * 10.0 ** rng.uniform(-4, 8, size=4096)).astype(np.float32)
+    sw = x.reshape(-1, 2)[:, ::-1].reshape(-1).copy()
+    assert oracle.ordered_sum_f32(sw, "ordered_tree") == oracle.ordered_sum_f32(x, "ordered_tree")
+    assert oracle.ordered_sum_f32(sw, "ordered_fold") != oracle.ordered_sum_f32(x, "ordered_fold")
+
+
+@pytest.mark.parametrize("pol", ORDERED)
+def test_ordered_sums_exact_on_integers_and_within_bound(pol):
+    rng = np.random.default_rng(14)
+    k = rng.integers(-1000, 1001, size=5000)
+    assert oracle.ordered_sum_f32(k.astype(np.float32), pol) == float(k.sum())
+    for n in (3, 1000, 65536):
+        x = rng.normal(size=n).astype(np.float32)
+        exact = math.fsum(float(v) for v in x)
+        steps = math.ceil(math.log2(n)) if pol == "ordered_tree" else n - 1
+        g = steps * 2.0 ** -24 / (1 - steps * 2.0 ** -24)
+        assert abs(oracle.ordered_sum_f32(x, pol) - exact) <= g * float(np.abs(x.astype(np.float64)).sum())
+
+
+@pytest.mark.parametrize("pol", ORDERED)
+def test_ordered_norm_replays(pol):
+    x = _rand(5, 1537, mean=3.0, std=2.0)
+    g = synth.uniform_f32(0, 1, 1537, 0.5, 1.5)
+    b = synth.normal_f32(0, 2, 1537, 0.0, 0.1)
+    # fold_left replays agree with the earlier (pinned) fold replays bit for bit
+    if pol == "ordered_fold":
+        assert np.array_equal(oracle.rmsnorm_ordered_f32(x, g, 1e-6, pol), oracle.rmsnorm_fold_f32(x, g, 1e-6))
+        assert np.array_equal(oracle.layernorm_ordered_f32(x, g, b, 1e-5, pol), oracle.layernorm_fold_f32(x, g, b, 1e-5))
+    # every replay is within FP32 rounding of the double definition
+    np.testing.assert_allclose(oracle.rmsnorm_ordered_f32(x, g, 1e-6, pol), oracle.rmsnorm(x, g, 1e-6), rtol=2e-5, atol=1e-6)
+    np.testing.assert_allclose(oracle.layernorm_ordered_f32(x, g, b, 1e-5, pol), oracle.layernorm(x, g, b, 1e-5),
+                               rtol=5e-4, atol=5e-5)
+    # constant rows: RMSNorm gives gamma*sign exactly at eps = 0 (c = 2^k), LayerNorm gives beta
+    c = np.full((2, 1537), -4.0, np.float32)
+    assert np.array_equal(oracle.rmsnorm_ordered_f32(c, g, 0.0, pol), np.tile(-g, (2, 1)))
+    assert np.array_equal(oracle.layernorm_ordered_f32(c, g, b, 1e-5, pol), np.tile(b, (2, 1)))
+    # the three policies generally disagree in the last bits (the order is observable)
+    if pol != "ordered_fold":
+        y = oracle.layernorm_ordered_f32(x, g, b, 1e-5, pol)
+        assert not np.array_equal(y, oracle.layernorm_ordered_f32(x, g, b, 1e-5, "ordered_fold"))
+
+
 def test_fold_replay_rows_are_independent():
     inp = synth.layernorm_inputs(5, 300, seed=4)
     full = oracle.layernorm_fold_f32(inp["x"], inp["gamma"], inp["beta"], 1e-5)
