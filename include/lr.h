@@ -32,15 +32,10 @@
  *           back to the CPU.  An explicit plan that cannot be realised
  *           returns LR_ERR_UNREALIZABLE_PLAN; it is never clamped.
  * Threads.  All entry points are thread-safe.
- * Policy.   LR_UNORDERED_TREE lets every add/max fold be reassociated (lane
- *           stripes, then a wave64 tree, then a cross-wave tree) and lets the
- *           kernels use hardware exp/rcp/rsqrt; results are still bitwise
- *           repeatable for a fixed plan.  LR_ORDERED_FOLD makes every add
- *           fold one FP32 left-to-right chain per row (j = 0 .. cols-1, each
- *           operation rounded on its own, no fused multiply-add), uses IEEE
- *           division and square root, and fixes the elementwise order; its
- *           result does not depend on the plan.  Max folds are exact in any
- *           order under both policies.
+ * Policy.   See lr_reduction_policy below: LR_UNORDERED_TREE lets every
+ *           add fold be reassociated; the three ordered policies fix the
+ *           order of every add fold, round every operation on its own and
+ *           give results that do not depend on the plan.
  */
 #ifndef LR_H
 #define LR_H
@@ -54,9 +49,27 @@ extern "C" {
 struct ihipStream_t;
 typedef struct ihipStream_t* hipStream_t;
 
+/* ReductionPolicy ("TIRx Metal reduction lowering", section 1): the order in
+ * which each add fold may be evaluated.  Max and min folds are exact in any
+ * order under every policy.
+ *   LR_UNORDERED_TREE  any order (lane stripes, wave trees); hardware
+ *                      exp/log/rcp/rsqrt; repeatable for a fixed plan.
+ *   LR_ORDERED_FOLD    fold_left: one FP32 chain j = 0 .. cols-1 from +0.0f.
+ *   LR_ORDERED_TREE    the pairwise tree in index order over the row's
+ *                      contributions padded with +0.0f to the next power of
+ *                      two (adjacent pairs added level by level).
+ *   LR_FOLD_RIGHT      one FP32 chain j = cols-1 .. 0 from +0.0f
+ *                      (acc = c_j + acc).
+ * Under the three ordered policies every operation is rounded on its own (no
+ * fused multiply-add), division and square root are IEEE, exp and log are
+ * the precise library functions, and the result does not depend on the
+ * plan. */
 typedef enum lr_reduction_policy {
     LR_UNORDERED_TREE = 0,
-    LR_ORDERED_FOLD = 1
+    LR_ORDERED_FOLD = 1,
+    LR_ORDERED_TREE = 2,
+    LR_FOLD_RIGHT = 3,
+    LR_FOLD_LEFT = LR_ORDERED_FOLD
 } lr_reduction_policy;
 
 typedef enum lr_status {
@@ -89,12 +102,18 @@ typedef enum lr_op {
  * STREAM:  no register copy; passes that need the row again reload it
  *          (softmax and cross-entropy fold max and sum-of-exp in one
  *          online pass).  Any row length.
- * ORDERED: the LR_ORDERED_FOLD realisation: one wavefront per row, the row
- *          staged through LDS in 256-element slabs and folded in order. */
+ * ORDERED: the ordered policies for any row: one wavefront per row, the row
+ *          staged through LDS in 256-element slabs, folded in order
+ *          (LR_ORDERED_FOLD, LR_FOLD_RIGHT) or summed as the pairwise tree
+ *          (LR_ORDERED_TREE).
+ * TREE:    LR_ORDERED_TREE on the CACHE layout, for rows whose start is
+ *          16-byte aligned and cols <= 32768: each wave's 256-element slab
+ *          is one wave tree, and the slab sums one more. */
 typedef enum lr_family {
     LR_FAMILY_CACHE = 0,
     LR_FAMILY_STREAM = 1,
-    LR_FAMILY_ORDERED = 2
+    LR_FAMILY_ORDERED = 2,
+    LR_FAMILY_TREE = 3
 } lr_family;
 
 /* A launch plan (the pages' GroupPlan decision record, section 2, mapped to
@@ -204,8 +223,9 @@ lr_status lr_row_minmax_f32(const float* x, float* mins, float* maxs, int64_t ro
 
 /* The same operations under an explicit plan (the pages' exact
  * thread/packing constraints, section 6: honoured exactly or rejected).
- * `plan->family` must be LR_FAMILY_ORDERED exactly when policy is
- * LR_ORDERED_FOLD.  A plan that does not cover the row, exceeds a device
+ * `plan->family` must match the policy: CACHE or STREAM for
+ * LR_UNORDERED_TREE, ORDERED for LR_ORDERED_FOLD and LR_FOLD_RIGHT, TREE or
+ * ORDERED for LR_ORDERED_TREE.  A plan that does not cover the row, exceeds a device
  * limit or names a chunk count with no compiled instance returns
  * LR_ERR_UNREALIZABLE_PLAN before any launch. */
 lr_status lr_softmax_f32_with_plan(const float* x, float* y, int64_t rows, int64_t cols,

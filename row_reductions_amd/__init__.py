@@ -21,8 +21,12 @@ LIB_PATH = os.path.join(_HERE, "liblr.so")
 
 # lr_reduction_policy
 LR_UNORDERED_TREE = 0
-LR_ORDERED_FOLD = 1
-POLICIES = {"unordered_tree": LR_UNORDERED_TREE, "ordered_fold": LR_ORDERED_FOLD}
+LR_ORDERED_FOLD = 1  # fold_left
+LR_ORDERED_TREE = 2
+LR_FOLD_RIGHT = 3
+LR_FOLD_LEFT = LR_ORDERED_FOLD
+POLICIES = {"unordered_tree": LR_UNORDERED_TREE, "ordered_fold": LR_ORDERED_FOLD, "fold_left": LR_FOLD_LEFT,
+            "ordered_tree": LR_ORDERED_TREE, "fold_right": LR_FOLD_RIGHT}
 
 # lr_op
 LR_OP_SOFTMAX, LR_OP_RMSNORM, LR_OP_LAYERNORM, LR_OP_CROSS_ENTROPY = 0, 1, 2, 3
@@ -32,8 +36,8 @@ OPS = {"softmax": LR_OP_SOFTMAX, "rmsnorm": LR_OP_RMSNORM, "layernorm": LR_OP_LA
        "row_sum": LR_OP_ROW_SUM, "row_minmax": LR_OP_ROW_MINMAX}
 
 # lr_family
-LR_FAMILY_CACHE, LR_FAMILY_STREAM, LR_FAMILY_ORDERED = 0, 1, 2
-FAMILY_NAMES = {0: "cache", 1: "stream", 2: "ordered"}
+LR_FAMILY_CACHE, LR_FAMILY_STREAM, LR_FAMILY_ORDERED, LR_FAMILY_TREE = 0, 1, 2, 3
+FAMILY_NAMES = {0: "cache", 1: "stream", 2: "ordered", 3: "tree"}
 
 # lr_status
 STATUS = {

@@ -30,9 +30,10 @@ COMMON = [
 
 # Per-source extra flags.  The ordered-fold kernels must round every
 # operation on its own and use IEEE division and square root.
-EXTRA = {
-    "k_ordered.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt"],
-}
+ORDERED_FLAGS = ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt"]
+TREE_OPS = ["softmax", "cross_entropy", "rmsnorm", "layernorm", "add_layernorm", "row_sum", "row_minmax"]
+EXTRA = {"k_ordered.hip": ORDERED_FLAGS}
+EXTRA.update({f"k_tree_{op}.hip": ORDERED_FLAGS for op in TREE_OPS})
 
 SOURCES = [
     "lr_abi.cpp",
@@ -45,6 +46,7 @@ SOURCES = [
     "k_row_sum.hip",
     "k_row_minmax.hip",
     "k_ordered.hip",
+    *[f"k_tree_{op}.hip" for op in TREE_OPS],
 ]
 
 

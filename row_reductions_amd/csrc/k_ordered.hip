@@ -1,17 +1,28 @@
-// ORDERED family: the ordered_fold policy (the pages' fold_left restriction,
-// "TIRx Metal reduction lowering", section 1): every add fold of a row is one
-// FP32 chain taken left to right, j = 0 .. cols-1, from the identity +0.0f,
-// with each multiply and add rounded on its own; division and square root
-// are IEEE (built with -ffp-contract=off and correctly rounded divide/sqrt);
-// max folds are exact and use the wave tree.  The result does not depend on
-// the plan, and RMSNorm / LayerNorm results are the unique FP32 values of the
-// stated operation sequence.
+// ORDERED family: the ordered reduction policies of "TIRx Metal reduction
+// lowering", section 1, for any row:
+//   fold_left (LR_ORDERED_FOLD): every add fold of a row is one FP32 chain
+//       taken left to right, j = 0 .. cols-1, from the identity +0.0f;
+//   fold_right: the same chain taken from the right end, acc = c_j + acc,
+//       j = cols-1 .. 0;
+//   ordered_tree: the pairwise tree in index order over the contributions
+//       padded with +0.0f to the next power of two.
+// Each multiply and add is rounded on its own; division and square root are
+// IEEE (built with -ffp-contract=off and correctly rounded divide/sqrt); max
+// and min folds are exact and use the wave tree.  The result does not depend
+// on the plan, and RMSNorm / LayerNorm / row-sum results are the unique FP32
+// values of the stated operation sequence.
 //
 // One wavefront owns a row.  Per 256-element slab, each lane loads four
 // elements (coalesced 32-bit loads at 64*i + lane), computes their
 // contributions elementwise in parallel and writes them to the wave's LDS
-// slab; then every lane folds the slab in order from LDS (broadcast reads),
-// so the serial chain costs one dependent add per element.
+// slab.  Folds: every lane folds the slab in order from LDS (broadcast
+// reads), one dependent add per element.  Tree: lane l reads slab entries
+// 4l .. 4l+3 and adds them pairwise, and the wave64 all-reduce -- whose steps
+// combine aligned adjacent lane blocks -- completes the slab's 256-leaf tree;
+// slab sums are then merged like a binary counter on a small LDS stack (two
+// adjacent complete subtrees of equal size merge at once), and the partial
+// subtrees left at the end are added from the smallest up, which is the tree
+// over the zero-padded row.
 #pragma clang fp contract(off)
 
 #include "lr_device.hpp"
@@ -46,36 +57,73 @@ __device__ __forceinline__ float row_elem(const float* xr, const float* rr, int 
     return rr ? xr[e] + rr[e] : xr[e];
 }
 
-// acc_{j+1} = acc_j + c(x_j), j = 0 .. cols-1, in FP32, identical in all lanes.
-template <int C>
-__device__ float ordered_fold(const float* xr, const float* rr, int cols, float ref, float* slab, int lane) {
+// The FP32 sum of c(x_j), j = 0 .. cols-1, in the order of policy POL,
+// identical in all lanes.  `stk`: this wave's tree stack (kTreeStack floats).
+template <int C, int POL>
+__device__ float ordered_sum(const float* xr, const float* rr, int cols, float ref, float* slab, float* stk,
+                             int lane) {
+    const int nslab = (cols + kSlab - 1) / kSlab;
     float acc = 0.0f;
-    for (int base = 0; base < cols; base += kSlab) {
-        const int slab_id = base / kSlab;
+    int depth = 0;           // tree: subtrees on the stack
+    unsigned done = 0;       // tree: slabs merged so far
+    for (int t = 0; t < nslab; ++t) {
+        const int slab_id = POL == kPolFoldRight ? nslab - 1 - t : t;
+        const int base = slab_id * kSlab;
 #pragma unroll
         for (int i = 0; i < kSlab / kWave; ++i) {
             const int e = ordered_elem(slab_id, i, lane);
             if (e < cols) slab[kWave * i + lane] = contrib<C>(row_elem(xr, rr, e), ref);
+            else if (POL == kPolTree) slab[kWave * i + lane] = 0.0f;  // padding: the add identity
         }
         wave_sync();
         const int n = min(kSlab, cols - base);
-        int j = 0;
-        for (; j + 4 <= n; j += 4) {
-            const float4 c = *reinterpret_cast<const float4*>(slab + j);
-            acc = acc + c.x;
-            acc = acc + c.y;
-            acc = acc + c.z;
-            acc = acc + c.w;
+        if constexpr (POL == kPolFoldLeft) {
+            int j = 0;
+            for (; j + 4 <= n; j += 4) {
+                const float4 c = *reinterpret_cast<const float4*>(slab + j);
+                acc = acc + c.x;
+                acc = acc + c.y;
+                acc = acc + c.z;
+                acc = acc + c.w;
+            }
+            for (; j < n; ++j) acc = acc + slab[j];
+        } else if constexpr (POL == kPolFoldRight) {
+            int j = n;
+            while (j % 4 != 0) {
+                --j;
+                acc = slab[j] + acc;
+            }
+            for (; j >= 4; j -= 4) {
+                const float4 c = *reinterpret_cast<const float4*>(slab + j - 4);
+                acc = c.w + acc;
+                acc = c.z + acc;
+                acc = c.y + acc;
+                acc = c.x + acc;
+            }
+        } else {  // kPolTree
+            const float4 q = *reinterpret_cast<const float4*>(slab + kVec * lane);
+            float s = wave_allreduce<AddOp>((q.x + q.y) + (q.z + q.w));
+            for (unsigned c = done; c & 1u; c >>= 1) s = stk[--depth] + s;  // left sibling + right
+            wave_sync();
+            if (lane == 0) stk[depth] = s;
+            ++depth;
+            ++done;
         }
-        for (; j < n; ++j) acc = acc + slab[j];
         wave_sync();
+    }
+    if constexpr (POL == kPolTree) {
+        // partial subtrees, largest first: add from the smallest up (each one's
+        // missing right sibling is all padding, an exact +0)
+        acc = stk[depth - 1];
+        for (int k = depth - 2; k >= 0; --k) acc = stk[k] + acc;
     }
     return acc;
 }
 
-template <int OP>
+template <int OP, int POL>
 __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
     __shared__ __attribute__((aligned(16))) float slabs[kMaxWaves][kSlab];
+    __shared__ float stacks[kMaxWaves][kTreeStack];
     const int lane = (int)threadIdx.x % kWave;
     const int wave = (int)threadIdx.x / kWave;
     const int64_t row = row_of(blockIdx.x, a.Q, wave);
@@ -83,13 +131,14 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
     const int cols = a.cols;
     const float* xr = a.x + row * (int64_t)cols;
     float* slab = slabs[wave];
+    float* stk = stacks[wave];
     const float n = (float)cols;
 
     if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
         float m = -INFINITY;
         for (int e = lane; e < cols; e += kWave) m = fmaxf(m, xr[e]);
         m = wave_allreduce<MaxOp>(m);
-        const float s = ordered_fold<kExpShift>(xr, nullptr, cols, m, slab, lane);
+        const float s = ordered_sum<kExpShift, POL>(xr, nullptr, cols, m, slab, stk, lane);
         if constexpr (OP == kCrossEntropy) {
             if (lane == 0) {
                 const int64_t lab = a.labels[row];
@@ -101,7 +150,7 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
             for (int e = lane; e < cols; e += kWave) yr[e] = expf(xr[e] - m) / s;
         }
     } else if constexpr (OP == kRowSum) {
-        const float sum = ordered_fold<kValue>(xr, nullptr, cols, 0.0f, slab, lane);
+        const float sum = ordered_sum<kValue, POL>(xr, nullptr, cols, 0.0f, slab, stk, lane);
         if (lane == 0) a.sums[row] = sum;
     } else if constexpr (OP == kRowMinMax) {
         // exact in any order: the wave tree, as the max fold above
@@ -117,7 +166,7 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
             if (a.maxs) a.maxs[row] = hi;
         }
     } else if constexpr (OP == kRmsNorm) {
-        const float ss = ordered_fold<kSquare>(xr, nullptr, cols, 0.0f, slab, lane);
+        const float ss = ordered_sum<kSquare, POL>(xr, nullptr, cols, 0.0f, slab, stk, lane);
         const float ms = ss / n;
         const float r = 1.0f / sqrtf(ms + a.eps);
         float* yr = a.y + row * (int64_t)cols;
@@ -127,8 +176,8 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
         }
     } else {  // LayerNorm; fused residual LayerNorm folds over x + residual
         const float* rr = OP == kAddLayerNorm ? a.residual + row * (int64_t)cols : nullptr;
-        const float mu = ordered_fold<kValue>(xr, rr, cols, 0.0f, slab, lane) / n;
-        const float var = ordered_fold<kCentredSquare>(xr, rr, cols, mu, slab, lane) / n;
+        const float mu = ordered_sum<kValue, POL>(xr, rr, cols, 0.0f, slab, stk, lane) / n;
+        const float var = ordered_sum<kCentredSquare, POL>(xr, rr, cols, mu, slab, stk, lane) / n;
         const float r = 1.0f / sqrtf(var + a.eps);
         float* yr = a.y + row * (int64_t)cols;
         float* sr = (OP == kAddLayerNorm && a.sum_out) ? a.sum_out + row * (int64_t)cols : nullptr;
@@ -145,19 +194,29 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
     }
 }
 
-hipError_t launch_ordered(int op, const KArgs& a, const lr_plan& p, hipStream_t s) {
+template <int POL>
+hipError_t launch_ordered_pol(int op, const KArgs& a, const lr_plan& p, hipStream_t s) {
     const dim3 grid((unsigned)p.blocks), block(p.threads_per_block);
     switch (op) {
-        case kSoftmax: hipLaunchKernelGGL(k_ordered<kSoftmax>, grid, block, 0, s, a); break;
-        case kRmsNorm: hipLaunchKernelGGL(k_ordered<kRmsNorm>, grid, block, 0, s, a); break;
-        case kLayerNorm: hipLaunchKernelGGL(k_ordered<kLayerNorm>, grid, block, 0, s, a); break;
-        case kCrossEntropy: hipLaunchKernelGGL(k_ordered<kCrossEntropy>, grid, block, 0, s, a); break;
-        case kAddLayerNorm: hipLaunchKernelGGL(k_ordered<kAddLayerNorm>, grid, block, 0, s, a); break;
-        case kRowSum: hipLaunchKernelGGL(k_ordered<kRowSum>, grid, block, 0, s, a); break;
-        case kRowMinMax: hipLaunchKernelGGL(k_ordered<kRowMinMax>, grid, block, 0, s, a); break;
+        case kSoftmax: hipLaunchKernelGGL((k_ordered<kSoftmax, POL>), grid, block, 0, s, a); break;
+        case kRmsNorm: hipLaunchKernelGGL((k_ordered<kRmsNorm, POL>), grid, block, 0, s, a); break;
+        case kLayerNorm: hipLaunchKernelGGL((k_ordered<kLayerNorm, POL>), grid, block, 0, s, a); break;
+        case kCrossEntropy: hipLaunchKernelGGL((k_ordered<kCrossEntropy, POL>), grid, block, 0, s, a); break;
+        case kAddLayerNorm: hipLaunchKernelGGL((k_ordered<kAddLayerNorm, POL>), grid, block, 0, s, a); break;
+        case kRowSum: hipLaunchKernelGGL((k_ordered<kRowSum, POL>), grid, block, 0, s, a); break;
+        case kRowMinMax: hipLaunchKernelGGL((k_ordered<kRowMinMax, POL>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_ordered(int op, int policy, const KArgs& a, const lr_plan& p, hipStream_t s) {
+    switch (policy) {
+        case kPolFoldLeft: return launch_ordered_pol<kPolFoldLeft>(op, a, p, s);
+        case kPolTree: return launch_ordered_pol<kPolTree>(op, a, p, s);
+        case kPolFoldRight: return launch_ordered_pol<kPolFoldRight>(op, a, p, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace lr

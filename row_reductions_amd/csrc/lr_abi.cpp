@@ -77,7 +77,7 @@ struct Call {
 };
 
 lr_status validate_call(const Call& c) {
-    if (c.policy != LR_UNORDERED_TREE && c.policy != LR_ORDERED_FOLD) return LR_ERR_INVALID_POLICY;
+    if (c.policy < LR_UNORDERED_TREE || c.policy > LR_FOLD_RIGHT) return LR_ERR_INVALID_POLICY;
     const bool ce = c.op == LR_OP_CROSS_ENTROPY;
     const bool res = c.op == LR_OP_ADD_LAYERNORM;
     const bool per_row = ce || c.op == LR_OP_ROW_SUM || c.op == LR_OP_ROW_MINMAX;  // one value per row out
@@ -187,7 +187,17 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     (void)hipGetLastError();  // clear a stale error so the launch's own status is seen
     hipError_t e;
     if (plan.family == LR_FAMILY_ORDERED) {
-        e = launch_ordered(c.op, a, plan, stream);
+        e = launch_ordered(c.op, c.policy, a, plan, stream);
+    } else if (plan.family == LR_FAMILY_TREE) {
+        switch (c.op) {
+            case LR_OP_SOFTMAX: e = launch_tree_softmax(a, plan, aligned, stream); break;
+            case LR_OP_RMSNORM: e = launch_tree_rmsnorm(a, plan, aligned, stream); break;
+            case LR_OP_LAYERNORM: e = launch_tree_layernorm(a, plan, aligned, stream); break;
+            case LR_OP_ADD_LAYERNORM: e = launch_tree_add_layernorm(a, plan, aligned, stream); break;
+            case LR_OP_ROW_SUM: e = launch_tree_row_sum(a, plan, aligned, stream); break;
+            case LR_OP_ROW_MINMAX: e = launch_tree_row_minmax(a, plan, aligned, stream); break;
+            default: e = launch_tree_cross_entropy(a, plan, aligned, stream); break;
+        }
     } else {
         switch (c.op) {
             case LR_OP_SOFTMAX: e = launch_softmax(a, plan, aligned, stream); break;

@@ -54,6 +54,17 @@ hipError_t launch_cross_entropy(const KArgs& a, const lr_plan& p, bool aligned, 
 hipError_t launch_add_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_row_sum(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_row_minmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
-hipError_t launch_ordered(int op, const KArgs& a, const lr_plan& p, hipStream_t s);
+hipError_t launch_ordered(int op, int policy, const KArgs& a, const lr_plan& p, hipStream_t s);
+// TREE family (ordered_tree on the cache layout), one translation unit per op.
+hipError_t launch_tree_softmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_tree_cross_entropy(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_tree_rmsnorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_tree_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_tree_add_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_tree_row_sum(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+hipError_t launch_tree_row_minmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+
+// Longest row the TREE family takes (128 slabs of 256 floats).
+constexpr int kTreeMaxCols = 128 * 256;
 
 }  // namespace lr

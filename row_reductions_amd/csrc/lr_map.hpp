@@ -26,6 +26,10 @@ constexpr int kWave = 64;       // lanes per wavefront (gfx950)
 constexpr int kVec = 4;         // floats per 128-bit chunk
 constexpr int kMaxWaves = 16;   // 1024 threads per workgroup
 constexpr int kSlab = 256;      // ordered family: floats folded per LDS slab
+constexpr int kTreeStack = 32;  // ordered family, tree policy: subtrees kept per wave (2^32 slabs)
+
+// Ordered reduction policies (the lr_reduction_policy codes).
+enum Policy : int { kPolUnordered = 0, kPolFoldLeft = 1, kPolTree = 2, kPolFoldRight = 3 };
 
 struct Team {
     int q;     // packed row within the workgroup

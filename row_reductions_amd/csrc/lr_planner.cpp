@@ -51,13 +51,25 @@ static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_
     p.threads_per_block = kWave * S * Q;
     p.blocks = (rows + Q - 1) / Q;
     p.reductions = reductions_of(op);
-    p.lds_bytes = family == LR_FAMILY_ORDERED ? Q * kSlab * 4 : 2 * kMaxWaves * 4;
+    p.lds_bytes = family == LR_FAMILY_ORDERED ? Q * (kSlab + kTreeStack) * 4
+                  : family == LR_FAMILY_TREE  ? 2 * kMaxWaves * 4 + 2 * kMaxWaves * 128 * 4
+                                              : 2 * kMaxWaves * 4;
     p.row_aligned = aligned ? 1 : 0;
     return p;
 }
 
 static bool valid_op(int op) { return op >= LR_OP_SOFTMAX && op <= LR_OP_ROW_MINMAX; }
-static bool valid_policy(int p) { return p == LR_UNORDERED_TREE || p == LR_ORDERED_FOLD; }
+static bool valid_policy(int p) { return p >= LR_UNORDERED_TREE && p <= LR_FOLD_RIGHT; }
+
+// Families a policy may run on: unordered -> CACHE, STREAM; fold_left and
+// fold_right -> ORDERED; ordered_tree -> TREE, ORDERED.
+static bool family_allowed(int policy, int family) {
+    switch (policy) {
+        case LR_UNORDERED_TREE: return family == LR_FAMILY_CACHE || family == LR_FAMILY_STREAM;
+        case LR_ORDERED_TREE: return family == LR_FAMILY_TREE || family == LR_FAMILY_ORDERED;
+        default: return family == LR_FAMILY_ORDERED;
+    }
+}
 
 static lr_status check_problem(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy) {
     if (f == nullptr) return LR_ERR_NULL_POINTER;
@@ -80,9 +92,12 @@ lr_status validate_plan(const lr_device_facts* f, int op, int64_t rows, int64_t 
         return LR_ERR_UNREALIZABLE_PLAN;
     const int64_t blocks = (rows + Q - 1) / Q;
     if (p->blocks != blocks || blocks > INT32_MAX) return LR_ERR_UNREALIZABLE_PLAN;
-    const bool ordered = policy == LR_ORDERED_FOLD;
-    if (ordered != (p->family == LR_FAMILY_ORDERED)) return LR_ERR_UNREALIZABLE_PLAN;
+    if (!family_allowed(policy, p->family)) return LR_ERR_UNREALIZABLE_PLAN;
     switch (p->family) {
+        case LR_FAMILY_TREE:
+            // the cache layout with aligned rows; at most 128 slabs of 256 floats
+            if (!aligned || cols > kTreeMaxCols) return LR_ERR_UNREALIZABLE_PLAN;
+            [[fallthrough]];
         case LR_FAMILY_CACHE: {
             if (p->vec != kVec || !cache_chunks_compiled(p->chunks_per_lane)) return LR_ERR_UNREALIZABLE_PLAN;
             const int64_t need = (max_row_chunks(cols, aligned) + kWave * S - 1) / (kWave * S);
@@ -110,11 +125,19 @@ static int enumerate_all(const lr_device_facts* f, int op, int64_t rows, int64_t
         if (out != nullptr && n < cap) out[n] = p;
         ++n;
     };
-    if (policy == LR_ORDERED_FOLD) {
+    const int64_t nv = max_row_chunks(cols, aligned);
+    if (policy != LR_UNORDERED_TREE) {
+        if (policy == LR_ORDERED_TREE) {
+            for (int S = 1; S <= kMaxWaves; ++S) {
+                const int nch = smallest_cache_instance((nv + kWave * S - 1) / (kWave * S));
+                if (nch == 0) continue;
+                for (int Q = 1; S * Q <= kMaxWaves; ++Q)
+                    push(make_plan(LR_FAMILY_TREE, S, Q, nch, rows, cols, op, aligned));
+            }
+        }
         for (int Q = 1; Q <= kMaxWaves; ++Q) push(make_plan(LR_FAMILY_ORDERED, 1, Q, 0, rows, cols, op, aligned));
         return n;
     }
-    const int64_t nv = max_row_chunks(cols, aligned);
     for (int S = 1; S <= kMaxWaves; ++S) {
         const int64_t need = (nv + kWave * S - 1) / (kWave * S);
         const int nch = smallest_cache_instance(need);
@@ -165,16 +188,21 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
         }
     }
     const int64_t simds = (int64_t)f->compute_units * (f->simds_per_cu > 0 ? f->simds_per_cu : 4);
-    if (policy == LR_ORDERED_FOLD) {
-        const int Q = rows >= 4 * simds ? 4 : 1;
-        return make_plan(LR_FAMILY_ORDERED, 1, Q, 0, rows, cols, op, aligned);
-    }
     const int64_t nv = max_row_chunks(cols, aligned);
     const int64_t target_waves = 2 * simds;
     auto need = [&](int s) { return (nv + kWave * s - 1) / (kWave * s); };
     int S = 1;
     while (S < kMaxWaves && (int64_t)rows * S < target_waves) ++S;
     while (S < kMaxWaves && need(S) > 8) ++S;
+    if (policy != LR_UNORDERED_TREE) {
+        // ordered_tree on aligned rows: the cache layout with the tree combine
+        if (policy == LR_ORDERED_TREE) {
+            lr_plan p = make_plan(LR_FAMILY_TREE, S, 1, smallest_cache_instance(need(S)), rows, cols, op, aligned);
+            if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
+        }
+        const int Q = rows >= 4 * simds ? 4 : 1;
+        return make_plan(LR_FAMILY_ORDERED, 1, Q, 0, rows, cols, op, aligned);
+    }
     int family = LR_FAMILY_CACHE;
     int nch = smallest_cache_instance(need(S));
     if (nch == 0 || (op == LR_OP_CROSS_ENTROPY && need(S) > 8)) {
@@ -265,7 +293,7 @@ extern "C" lr_status lr_coverage_check(const lr_plan* p, int64_t rows, int64_t c
                     if (elem_valid(e, c)) counts[row * cols + e] += 1;
                 }
             };
-            if (p->family == LR_FAMILY_CACHE) {
+            if (p->family == LR_FAMILY_CACHE || p->family == LR_FAMILY_TREE) {
                 for (int cc = 0; cc < p->chunks_per_lane; ++cc) visit(chunk_index(t.w, W, cc));
             } else {
                 const int U = p->chunks_per_lane;

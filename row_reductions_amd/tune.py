@@ -125,10 +125,11 @@ def main(argv=None):
           f"best {again:.2f} us ({moved / again / 1e3:.0f} GB/s): {best!r}")
     for us, p, rec in results[:8]:
         print(f"#   {us:8.2f} us  {p!r}")
-    fam = {0: "LR_FAMILY_CACHE", 1: "LR_FAMILY_STREAM", 2: "LR_FAMILY_ORDERED"}[best.family]
+    fam = {0: "LR_FAMILY_CACHE", 1: "LR_FAMILY_STREAM", 2: "LR_FAMILY_ORDERED", 3: "LR_FAMILY_TREE"}[best.family]
     opn = {0: "LR_OP_SOFTMAX", 1: "LR_OP_RMSNORM", 2: "LR_OP_LAYERNORM", 3: "LR_OP_CROSS_ENTROPY",
            4: "LR_OP_ADD_LAYERNORM", 5: "LR_OP_ROW_SUM", 6: "LR_OP_ROW_MINMAX"}[lr.OPS[op]]
-    pol = "LR_ORDERED_FOLD" if args.policy == "ordered_fold" else "LR_UNORDERED_TREE"
+    pol = {"unordered_tree": "LR_UNORDERED_TREE", "ordered_fold": "LR_ORDERED_FOLD", "fold_left": "LR_ORDERED_FOLD",
+           "ordered_tree": "LR_ORDERED_TREE", "fold_right": "LR_FOLD_RIGHT"}[args.policy]
     print(f"{{{opn}, {pol}, {rows}, {cols}, {aligned}, {fam}, {best.waves_per_row}, "
           f"{best.rows_per_block}, {best.chunks_per_lane}}},")
     return 0

@@ -59,7 +59,7 @@ def test_zero_rows_is_ok_without_launch():
     (lambda: lr.lr_softmax_f32(X, Y, 4, -3, 0, 0), lr.LR_ERR_INVALID_SHAPE),
     (lambda: lr.lr_softmax_f32(X, Y, 4, 1 << 24, 0, 0), lr.LR_ERR_INVALID_SHAPE),
     (lambda: lr.lr_softmax_f32(X, Y, 1 << 31, 8, 0, 0), lr.LR_ERR_INVALID_SHAPE),
-    (lambda: lr.lr_softmax_f32(X, Y, 4, 8, 2, 0), lr.LR_ERR_INVALID_POLICY),
+    (lambda: lr.lr_softmax_f32(X, Y, 4, 8, 4, 0), lr.LR_ERR_INVALID_POLICY),
     (lambda: lr.lr_softmax_f32(X, Y, 4, 8, -1, 0), lr.LR_ERR_INVALID_POLICY),
     (lambda: lr.lr_rmsnorm_f32(X, G, Y, 4, 8, float("nan"), 0, 0), lr.LR_ERR_INVALID_EPS),
     (lambda: lr.lr_rmsnorm_f32(X, G, Y, 4, 8, float("inf"), 0, 0), lr.LR_ERR_INVALID_EPS),
@@ -79,7 +79,7 @@ def test_zero_rows_is_ok_without_launch():
     (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, SUM, 4, 8, float("nan"), 0, 0), lr.LR_ERR_INVALID_EPS),
     (lambda: lr.lr_add_layernorm_f32(X, RES + 2, G, B, Y, SUM, 4, 8, 1e-5, 0, 0), lr.LR_ERR_MISALIGNED),
     (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, SUM + 1, 4, 8, 1e-5, 0, 0), lr.LR_ERR_MISALIGNED),
-    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, SUM, 4, 8, 1e-5, 3, 0), lr.LR_ERR_INVALID_POLICY),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, SUM, 4, 8, 1e-5, 7, 0), lr.LR_ERR_INVALID_POLICY),
     (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, RES + 4, None, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
     (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, Y + 16, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
     (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, Y, 4, 8, 1e-5, 0, 0), lr.LR_ERR_ALIASING),
@@ -92,6 +92,7 @@ def test_zero_rows_is_ok_without_launch():
     (lambda: lr.lr_row_sum_f32(X, LOSS + 2, 4, 8, 0, 0), lr.LR_ERR_MISALIGNED),
     (lambda: lr.lr_row_minmax_f32(X, None, LOSS + 1, 4, 8, 0, 0), lr.LR_ERR_MISALIGNED),
     (lambda: lr.lr_row_sum_f32(X, LOSS, 4, 8, 5, 0), lr.LR_ERR_INVALID_POLICY),
+    (lambda: lr.lr_add_layernorm_f32(X, RES, G, B, Y, SUM, 4, 8, 1e-5, 4, 0), lr.LR_ERR_INVALID_POLICY),
     (lambda: lr.lr_row_sum_f32(X, X + 64, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
     (lambda: lr.lr_row_minmax_f32(X, LOSS, LOSS + 8, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
     (lambda: lr.lr_row_minmax_f32(X, LOSS, LOSS, 4, 8, 0, 0), lr.LR_ERR_ALIASING),
@@ -114,6 +115,8 @@ def test_valid_call_without_device_reports_hip_error():
         pytest.skip("a GPU is present")
     assert lr.lr_softmax_f32(X, Y, 4, 8, 0, 0) == lr.LR_ERR_HIP
     assert lr.lr_softmax_f32(X, X, 4, 8, 0, 0) == lr.LR_ERR_HIP  # in place is allowed
+    for pol in (lr.LR_ORDERED_TREE, lr.LR_FOLD_RIGHT):  # every policy is accepted
+        assert lr.lr_softmax_f32(X, Y, 4, 8, pol, 0) == lr.LR_ERR_HIP
     # fused residual LayerNorm: outputs may be exactly x or the residual
     assert lr.lr_add_layernorm_f32(X, RES, G, B, X, RES, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP
     assert lr.lr_add_layernorm_f32(X, RES, None, None, RES, X, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP

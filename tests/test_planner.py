@@ -23,7 +23,10 @@ def coverage(plan, rows, cols, phase):
     return counts
 
 
-@pytest.mark.parametrize("policy", ["unordered_tree", "ordered_fold"])
+POLICIES = ["unordered_tree", "ordered_fold", "ordered_tree", "fold_right"]
+
+
+@pytest.mark.parametrize("policy", POLICIES)
 def test_every_plan_covers_each_element_once(policy):
     checked = 0
     for cols in WIDTHS:
@@ -52,24 +55,30 @@ def test_config_shapes_every_plan_covers_once():
 def test_plans_respect_device_limits():
     for op in OPS:
         for rows, cols in [(1, 1), (37, 1537), (768, 6144), (4096, 32000), (5, 100000)]:
-            for policy in ("unordered_tree", "ordered_fold"):
+            for policy in POLICIES:
                 for p in lr.lr_plan_enumerate(F, op, rows, cols, policy, 1 if cols % 4 == 0 else 0):
                     assert p.threads_per_block == 64 * p.waves_per_row * p.rows_per_block <= 1024
                     assert p.blocks == -(-rows // p.rows_per_block)
                     assert p.lds_bytes <= 64 * 1024
-                    if p.family == lr.LR_FAMILY_CACHE:
+                    if p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_TREE):
                         need = -(-((cols + 6) // 4 if cols % 4 else cols // 4) // (64 * p.waves_per_row))
                         assert p.chunks_per_lane >= need
                         assert p.chunks_per_lane in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32)
-                    if policy == "ordered_fold":
+                    if policy in ("ordered_fold", "fold_right"):
                         assert p.family == lr.LR_FAMILY_ORDERED and p.waves_per_row == 1
+                    if policy == "ordered_tree":
+                        assert p.family in (lr.LR_FAMILY_TREE, lr.LR_FAMILY_ORDERED)
+                        if p.family == lr.LR_FAMILY_TREE:
+                            assert cols % 4 == 0 and cols <= 32768
+                    if policy == "unordered_tree":
+                        assert p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_STREAM)
 
 
 def test_automatic_plan_is_legal_and_deterministic():
     for op in OPS:
         for rows, cols in [(37, 1537), (256, 3072), (64, 12289), (768, 6144), (4096, 32000), (7, 4096),
                            (1, 1), (100000, 64)]:
-            for policy in ("unordered_tree", "ordered_fold"):
+            for policy in POLICIES:
                 al = 1 if cols % 4 == 0 else 0
                 a = lr.lr_plan_for_device(F, op, rows, cols, policy, al)
                 b = lr.lr_plan_for_device(F, op, rows, cols, policy, al)
@@ -110,6 +119,21 @@ def test_ordered_policy_rejects_unordered_plan():
     q = lr.lr_plan_for_device(F, "rmsnorm", 256, 3072, "ordered_fold", 1)
     assert q.family == lr.LR_FAMILY_ORDERED
     assert lr.lr_plan_validate(F, "rmsnorm", 256, 3072, "unordered_tree", 1, q) == lr.LR_ERR_UNREALIZABLE_PLAN
+
+
+def test_tree_family_is_for_ordered_tree_on_aligned_rows_only():
+    q = lr.lr_plan_for_device(F, "layernorm", 768, 6144, "ordered_tree", 1)
+    assert q.family == lr.LR_FAMILY_TREE
+    for pol in ("unordered_tree", "ordered_fold", "fold_right"):
+        assert lr.lr_plan_validate(F, "layernorm", 768, 6144, pol, 1, q) == lr.LR_ERR_UNREALIZABLE_PLAN
+    assert lr.lr_plan_validate(F, "layernorm", 768, 6144, "ordered_tree", 0, q) == lr.LR_ERR_UNREALIZABLE_PLAN
+    # misaligned rows and rows past 128 slabs take the ordered family
+    assert lr.lr_plan_for_device(F, "layernorm", 64, 12289, "ordered_tree", 0).family == lr.LR_FAMILY_ORDERED
+    assert lr.lr_plan_for_device(F, "row_sum", 4, 32772, "ordered_tree", 1).family == lr.LR_FAMILY_ORDERED
+    assert lr.lr_plan_for_device(F, "row_sum", 4, 32768, "ordered_tree", 1).family == lr.LR_FAMILY_TREE
+    # an ordered plan serves ordered_tree too
+    o = lr.lr_plan_for_device(F, "layernorm", 768, 6144, "ordered_fold", 1)
+    assert lr.lr_plan_validate(F, "layernorm", 768, 6144, "ordered_tree", 1, o) == lr.LR_OK
 
 
 def test_cache_plan_for_aligned_rows_does_not_cover_misaligned_rows():
