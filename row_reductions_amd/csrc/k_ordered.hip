@@ -57,48 +57,93 @@ __device__ __forceinline__ float row_elem(const float* xr, const float* rr, int 
     return rr ? xr[e] + rr[e] : xr[e];
 }
 
+// Folds one full 256-entry slab into acc, left to right (FOLD_RIGHT: right to
+// left), one dependent add per entry; the LDS reads run a 16-float group
+// ahead of the adds so their latency hides behind the chain.
+template <int POL>
+__device__ __forceinline__ float fold_full_slab(const float* slab, float acc) {
+    const float4* s4 = reinterpret_cast<const float4*>(slab);
+    constexpr int G = kSlab / 16;  // groups of four float4
+    auto grp = [&](int g, float4 (&q)[4]) {
+        const int base = POL == kPolFoldRight ? 4 * (G - 1 - g) : 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = s4[base + i];
+    };
+    float4 cur[4], nxt[4];
+    grp(0, cur);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (g + 1 < G) grp(g + 1, nxt);
+        if constexpr (POL == kPolFoldRight) {
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                acc = cur[i].w + acc;
+                acc = cur[i].z + acc;
+                acc = cur[i].y + acc;
+                acc = cur[i].x + acc;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = acc + cur[i].x;
+                acc = acc + cur[i].y;
+                acc = acc + cur[i].z;
+                acc = acc + cur[i].w;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+    }
+    return acc;
+}
+
 // The FP32 sum of c(x_j), j = 0 .. cols-1, in the order of policy POL,
 // identical in all lanes.  `stk`: this wave's tree stack (kTreeStack floats).
+// The row is read through buffer resources (reads past the row return 0, so
+// the loads are unconditional), and the loads of the next three slabs are in
+// flight while the current slab is folded (a slab folds in well under an HBM
+// round trip under load).
 template <int C, int POL>
 __device__ float ordered_sum(const float* xr, const float* rr, int cols, float ref, float* slab, float* stk,
                              int lane) {
     const int nslab = (cols + kSlab - 1) / kSlab;
+    const BufRes rx = make_res(xr, cols * 4);
+    const BufRes rres = make_res(rr, rr ? cols * 4 : 0);
+    auto slab_of = [&](int t) { return POL == kPolFoldRight ? nslab - 1 - t : t; };
+    auto fetch = [&](int slab_id, float (&f)[kSlab / kWave]) {
+#pragma unroll
+        for (int i = 0; i < kSlab / kWave; ++i) {
+            const int e = ordered_elem(slab_id, i, lane);
+            f[i] = res_ld1(rx, e * 4);
+            if (rr) f[i] = f[i] + res_ld1(rres, e * 4);
+        }
+    };
     float acc = 0.0f;
     int depth = 0;           // tree: subtrees on the stack
     unsigned done = 0;       // tree: slabs merged so far
-    for (int t = 0; t < nslab; ++t) {
-        const int slab_id = POL == kPolFoldRight ? nslab - 1 - t : t;
+    // one slab: contributions to LDS, then fold / tree step
+    auto step = [&](int t, const float (&cur)[kSlab / kWave]) {
+        const int slab_id = slab_of(t);
         const int base = slab_id * kSlab;
 #pragma unroll
         for (int i = 0; i < kSlab / kWave; ++i) {
             const int e = ordered_elem(slab_id, i, lane);
-            if (e < cols) slab[kWave * i + lane] = contrib<C>(row_elem(xr, rr, e), ref);
-            else if (POL == kPolTree) slab[kWave * i + lane] = 0.0f;  // padding: the add identity
+            // past the row: the add identity (the tree's padding; never read by the folds)
+            slab[kWave * i + lane] = e < cols ? contrib<C>(cur[i], ref) : 0.0f;
         }
         wave_sync();
         const int n = min(kSlab, cols - base);
         if constexpr (POL == kPolFoldLeft) {
-            int j = 0;
-            for (; j + 4 <= n; j += 4) {
-                const float4 c = *reinterpret_cast<const float4*>(slab + j);
-                acc = acc + c.x;
-                acc = acc + c.y;
-                acc = acc + c.z;
-                acc = acc + c.w;
+            if (n == kSlab) {
+                acc = fold_full_slab<POL>(slab, acc);
+            } else {
+                for (int j = 0; j < n; ++j) acc = acc + slab[j];
             }
-            for (; j < n; ++j) acc = acc + slab[j];
         } else if constexpr (POL == kPolFoldRight) {
-            int j = n;
-            while (j % 4 != 0) {
-                --j;
-                acc = slab[j] + acc;
-            }
-            for (; j >= 4; j -= 4) {
-                const float4 c = *reinterpret_cast<const float4*>(slab + j - 4);
-                acc = c.w + acc;
-                acc = c.z + acc;
-                acc = c.y + acc;
-                acc = c.x + acc;
+            if (n == kSlab) {
+                acc = fold_full_slab<POL>(slab, acc);
+            } else {
+                for (int j = n - 1; j >= 0; --j) acc = slab[j] + acc;
             }
         } else {  // kPolTree
             const float4 q = *reinterpret_cast<const float4*>(slab + kVec * lane);
@@ -110,6 +155,24 @@ __device__ float ordered_sum(const float* xr, const float* rr, int cols, float r
             ++done;
         }
         wave_sync();
+    };
+    // four register buffers, unrolled, so that a buffer is refilled only after
+    // its slab was used (no copies of registers with loads in flight)
+    auto slab_or_end = [&](int t) { return t < nslab ? slab_of(t) : nslab; };  // past the end: zeros
+    float b0[kSlab / kWave], b1[kSlab / kWave], b2[kSlab / kWave], b3[kSlab / kWave];
+    fetch(slab_or_end(0), b0);
+    fetch(slab_or_end(1), b1);
+    fetch(slab_or_end(2), b2);
+    fetch(slab_or_end(3), b3);
+    for (int t = 0; t < nslab; t += 4) {
+        step(t, b0);
+        fetch(slab_or_end(t + 4), b0);
+        if (t + 1 < nslab) step(t + 1, b1);
+        fetch(slab_or_end(t + 5), b1);
+        if (t + 2 < nslab) step(t + 2, b2);
+        fetch(slab_or_end(t + 6), b2);
+        if (t + 3 < nslab) step(t + 3, b3);
+        fetch(slab_or_end(t + 7), b3);
     }
     if constexpr (POL == kPolTree) {
         // partial subtrees, largest first: add from the smallest up (each one's
