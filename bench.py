@@ -113,16 +113,16 @@ def main():
     lg = torch.from_numpy(ln["gamma"]).to(dev)
     lb = torch.from_numpy(ln["beta"]).to(dev)
 
-    def launch(op: str, i: int) -> None:
+    def launch(op: str, i: int, policy: int = lr.LR_UNORDERED_TREE) -> None:
         k = i % nsets
         if op == "softmax":
-            st = lr.lib.lr_softmax_f32(sx[k].data_ptr(), sy[k].data_ptr(), ROWS, COLS, 0, sh)
+            st = lr.lib.lr_softmax_f32(sx[k].data_ptr(), sy[k].data_ptr(), ROWS, COLS, policy, sh)
         elif op == "rmsnorm":
             st = lr.lib.lr_rmsnorm_f32(rx[k].data_ptr(), rg.data_ptr(), ry[k].data_ptr(), ROWS, COLS,
-                                       EPS["rmsnorm"], 0, sh)
+                                       EPS["rmsnorm"], policy, sh)
         else:
             st = lr.lib.lr_layernorm_f32(lx[k].data_ptr(), lg.data_ptr(), lb.data_ptr(), ly[k].data_ptr(),
-                                         ROWS, COLS, EPS["layernorm"], 0, sh)
+                                         ROWS, COLS, EPS["layernorm"], policy, sh)
         if st != 0:
             raise lr.LrError(st, op)
 
@@ -250,6 +250,19 @@ def main():
                 torch.cuda.synchronize()
                 us = a.elapsed_time(z) * 1e3 / n
                 extra[f"{op}_768x6144_warm"] = {"us_per_op": round(us, 3), "gbps": round(b / us / 1e3, 1)}
+        # the deterministic ordered_tree policy on the same step (cold)
+        for op in OPS:
+            for i in range(10):
+                launch(op, i, lr.LR_ORDERED_TREE)
+            torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(400):
+                launch(op, i, lr.LR_ORDERED_TREE)
+            z.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(z) * 1e3 / 400
+            extra[f"{op}_768x6144_ordered_tree_cold"] = {"us_per_op": round(us, 3), "gbps": round(b / us / 1e3, 1)}
         extra.update(add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets))
         ce = synth.cross_entropy_inputs(4096, 32000, seed=0)
         cx = [torch.from_numpy(ce["logits"]).to(dev)]
