@@ -332,7 +332,8 @@ def main():
 
 def small_configs_graph(lr, synth, torch, dev) -> dict:
     """The launch-bound workloads (softmax 37x1537, RMSNorm 256x3072 under both
-    listed policies, LayerNorm 64x12289): 200 launches captured in one HIP
+    listed policies, LayerNorm 64x12289 without and with a workspace for the
+    split-row kernels): 200 launches captured in one HIP
     graph and replayed, so the per-launch time is the GPU's, not the host's
     launch rate.  Inputs stay resident (one buffer set: these tensors fit in
     the L2s, as they do between a producer and this kernel in practice)."""
@@ -353,6 +354,11 @@ def small_configs_graph(lr, synth, torch, dev) -> dict:
     lg, lb = torch.from_numpy(lin["gamma"]).to(dev), torch.from_numpy(lin["beta"]).to(dev)
     ly = torch.empty_like(lx)
     cases.append(("layernorm_64x12289", lambda sh: lr.lr_layernorm_f32(lx, lg, lb, ly, 64, 12289, 1e-5, 0, sh),
+                  2 * lx.numel() * 4))
+    # the same with a workspace: rows split across workgroups (two kernels)
+    lws = torch.empty(lr.lr_workspace_query("layernorm", 64, 12289), dtype=torch.uint8, device=dev)
+    cases.append(("layernorm_64x12289_split",
+                  lambda sh: lr.lr_layernorm_f32(lx, lg, lb, ly, 64, 12289, 1e-5, 0, sh, workspace=lws),
                   2 * lx.numel() * 4))
     for name, fn, nbytes in cases:
         side = torch.cuda.Stream()

@@ -14,7 +14,9 @@
  * ---------------------------------------
  * Memory.   All tensor pointers are DEVICE pointers owned by the caller.  The
  *           library allocates no device memory, keeps no device state and
- *           never reads or writes outside the ranges described per call.
+ *           never reads or writes outside the ranges described per call
+ *           (the SPLIT family's partials go to a workspace the caller
+ *           passes to lr_run_f32).
  *           FP32 pointers must be 4-byte aligned and the int64 label pointer
  *           8-byte aligned (else LR_ERR_MISALIGNED); 16-byte alignment is not
  *           required (misaligned rows take a guarded path).
@@ -82,7 +84,8 @@ typedef enum lr_status {
     LR_ERR_ALIASING = 6,
     LR_ERR_UNREALIZABLE_PLAN = 7,
     LR_ERR_HIP = 8,
-    LR_ERR_INVALID_ARGUMENT = 9
+    LR_ERR_INVALID_ARGUMENT = 9,
+    LR_ERR_WORKSPACE = 10
 } lr_status;
 
 typedef enum lr_op {
@@ -108,12 +111,22 @@ typedef enum lr_op {
  *          (LR_ORDERED_TREE).
  * TREE:    LR_ORDERED_TREE on the CACHE layout, for rows whose start is
  *          16-byte aligned and cols <= 32768: each wave's 256-element slab
- *          is one wave tree, and the slab sums one more. */
+ *          is one wave tree, and the slab sums one more.
+ * SPLIT:   LR_UNORDERED_TREE for rows too few to fill the device: each row
+ *          is cut into `splits` segments of whole 16-byte chunks, one
+ *          workgroup per segment.  A first kernel writes every segment's
+ *          partial statistics (max and sum of exp, sum of squares, mean and
+ *          sum of squared deviations, sum, minimum and maximum) to a
+ *          workspace, and a second merges a row's partials and writes its
+ *          outputs, re-reading the segment from L2.  Needs a caller workspace
+ *          (lr_run_f32); the automatic plan of the other entry points never
+ *          splits rows. */
 typedef enum lr_family {
     LR_FAMILY_CACHE = 0,
     LR_FAMILY_STREAM = 1,
     LR_FAMILY_ORDERED = 2,
-    LR_FAMILY_TREE = 3
+    LR_FAMILY_TREE = 3,
+    LR_FAMILY_SPLIT = 4
 } lr_family;
 
 /* A launch plan (the pages' GroupPlan decision record, section 2, mapped to
@@ -125,14 +138,17 @@ typedef struct lr_plan {
     int32_t vec;               /* V: consecutive FP32 a lane owns per chunk (4 = 128-bit) */
     int32_t chunks_per_lane;   /* CACHE: 128-bit chunks held per lane (a compiled
                                   instance: 1,2,3,4,6,8,12,16,24 or 32);
+                                  SPLIT: chunks per lane of one segment
+                                  (1,2,3,4,6 or 8);
                                   STREAM: chunks loaded per lane per loop trip;
                                   ORDERED: 0 */
     int32_t threads_per_block; /* 64 * S * Q */
-    int64_t blocks;            /* ceil(rows / Q) */
+    int64_t blocks;            /* ceil(rows / Q); SPLIT: rows * splits */
     int32_t lds_bytes;         /* static LDS the kernel uses */
     int32_t reductions;        /* |R|: cross-lane reductions per row */
     int32_t row_aligned;       /* 1: planned for 16-byte aligned rows */
-    int32_t reserved;
+    int32_t splits;            /* SPLIT: segments per row, 2..64 (Q = 1);
+                                  0 for every other family */
 } lr_plan;
 
 /* What the planner needs to know about a device. */
@@ -223,7 +239,8 @@ lr_status lr_row_minmax_f32(const float* x, float* mins, float* maxs, int64_t ro
 
 /* The same operations under an explicit plan (the pages' exact
  * thread/packing constraints, section 6: honoured exactly or rejected).
- * `plan->family` must match the policy: CACHE or STREAM for
+ * `plan->family` must match the policy: CACHE or STREAM (or SPLIT, which
+ * needs lr_run_f32's workspace: LR_ERR_WORKSPACE here) for
  * LR_UNORDERED_TREE, ORDERED for LR_ORDERED_FOLD and LR_FOLD_RIGHT, TREE or
  * ORDERED for LR_ORDERED_TREE.  A plan that does not cover the row, exceeds a device
  * limit or names a chunk count with no compiled instance returns
@@ -256,6 +273,57 @@ lr_status lr_row_minmax_f32_with_plan(const float* x, float* mins, float* maxs, 
                                       const lr_plan* plan, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Every operation through one call, with an optional workspace
+ * ------------------------------------------------------------------------- */
+
+/* The tensors of an operation; members an operation does not use must be
+ * NULL.  Meanings, shapes and aliasing rules are those of the typed entry
+ * points above (x is the logits for LR_OP_CROSS_ENTROPY). */
+typedef struct lr_tensors {
+    const float* x;
+    const float* residual;   /* LR_OP_ADD_LAYERNORM */
+    const float* gamma;      /* norms, or NULL */
+    const float* beta;       /* LayerNorms, or NULL */
+    const int64_t* labels;   /* LR_OP_CROSS_ENTROPY */
+    float* y;                /* softmax and norms */
+    float* sum_out;          /* LR_OP_ADD_LAYERNORM, or NULL */
+    float* losses;           /* LR_OP_CROSS_ENTROPY */
+    float* sums;             /* LR_OP_ROW_SUM */
+    float* mins;             /* LR_OP_ROW_MINMAX, or NULL */
+    float* maxs;             /* LR_OP_ROW_MINMAX, or NULL */
+} lr_tensors;
+
+/* Runs `op` exactly as its typed entry point does, and may also use the
+ * SPLIT family, whose partial statistics live in `workspace`.
+ *   workspace:  device memory owned by the caller, 16-byte aligned
+ *               (LR_ERR_MISALIGNED), overlapping no tensor of the call
+ *               (LR_ERR_ALIASING); NULL when workspace_bytes is 0.  Its
+ *               contents on entry do not matter; the call overwrites the
+ *               first lr_plan_workspace_bytes(plan, rows) bytes (stream
+ *               order: the call's kernels finish with it before later
+ *               work on `stream`).  Calls that may run concurrently need
+ *               workspaces of their own.
+ *   plan NULL:  the automatic plan; it splits rows only when that is
+ *               faster and workspace_bytes >= lr_workspace_query's figure,
+ *               and otherwise equals the typed entry point's plan.
+ *   plan given: honoured exactly or rejected, as for the _with_plan calls;
+ *               a SPLIT plan with a smaller workspace returns LR_ERR_WORKSPACE.
+ * Unused members of `tensors` must be NULL (else LR_ERR_INVALID_ARGUMENT). */
+lr_status lr_run_f32(lr_op op, const lr_tensors* tensors, int64_t rows, int64_t cols, float eps,
+                     lr_reduction_policy policy, const lr_plan* plan, void* workspace,
+                     uint64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes lr_run_f32's automatic plan uses for this problem on the
+ * current device with a workspace available (0 when it does not split):
+ * the larger of the figures for 16-byte aligned and for misaligned rows. */
+lr_status lr_workspace_query(lr_op op, int64_t rows, int64_t cols, lr_reduction_policy policy,
+                             uint64_t* bytes);
+
+/* Workspace bytes `plan` needs for `rows` rows: rows * splits * 8 for a SPLIT
+ * plan, 0 for any other (and for a NULL plan). */
+uint64_t lr_plan_workspace_bytes(const lr_plan* plan, int64_t rows);
+
+/* ---------------------------------------------------------------------------
  * Planner (host only; no device memory touched)
  * ------------------------------------------------------------------------- */
 
@@ -272,12 +340,20 @@ lr_status lr_plan_query(lr_op op, int64_t rows, int64_t cols,
                         lr_reduction_policy policy, lr_plan* out);
 
 /* Pure planner: the automatic plan for `facts`.  row_aligned = 1 when every
- * row starts 16-byte aligned (cols % 4 == 0 and aligned bases). */
+ * row starts 16-byte aligned (cols % 4 == 0 and aligned bases).  Never a
+ * SPLIT plan (the typed entry points have no workspace). */
 lr_status lr_plan_for_device(const lr_device_facts* facts, lr_op op, int64_t rows,
                              int64_t cols, lr_reduction_policy policy,
                              int32_t row_aligned, lr_plan* out);
 
-/* Every legal plan, in enumeration order (family, S, Q).  Writes at most
+/* The automatic plan when a workspace is available: lr_plan_for_device's
+ * plan, or a SPLIT plan for rows too few to fill the device. */
+lr_status lr_plan_for_device_ws(const lr_device_facts* facts, lr_op op, int64_t rows,
+                                int64_t cols, lr_reduction_policy policy,
+                                int32_t row_aligned, lr_plan* out);
+
+/* Every legal plan, in enumeration order (family, S, Q; SPLIT plans last,
+ * for splits = 2, 4, .., 64 up to the row's chunk count).  Writes at most
  * `capacity` plans to `out` (out may be NULL when capacity is 0) and the
  * total number of legal plans to *count. */
 lr_status lr_plan_enumerate(const lr_device_facts* facts, lr_op op, int64_t rows,

@@ -36,14 +36,14 @@ OPS = {"softmax": LR_OP_SOFTMAX, "rmsnorm": LR_OP_RMSNORM, "layernorm": LR_OP_LA
        "row_sum": LR_OP_ROW_SUM, "row_minmax": LR_OP_ROW_MINMAX}
 
 # lr_family
-LR_FAMILY_CACHE, LR_FAMILY_STREAM, LR_FAMILY_ORDERED, LR_FAMILY_TREE = 0, 1, 2, 3
-FAMILY_NAMES = {0: "cache", 1: "stream", 2: "ordered", 3: "tree"}
+LR_FAMILY_CACHE, LR_FAMILY_STREAM, LR_FAMILY_ORDERED, LR_FAMILY_TREE, LR_FAMILY_SPLIT = 0, 1, 2, 3, 4
+FAMILY_NAMES = {0: "cache", 1: "stream", 2: "ordered", 3: "tree", 4: "split"}
 
 # lr_status
 STATUS = {
     0: "LR_OK", 1: "LR_ERR_NULL_POINTER", 2: "LR_ERR_INVALID_SHAPE", 3: "LR_ERR_INVALID_EPS",
     4: "LR_ERR_INVALID_POLICY", 5: "LR_ERR_MISALIGNED", 6: "LR_ERR_ALIASING",
-    7: "LR_ERR_UNREALIZABLE_PLAN", 8: "LR_ERR_HIP", 9: "LR_ERR_INVALID_ARGUMENT",
+    7: "LR_ERR_UNREALIZABLE_PLAN", 8: "LR_ERR_HIP", 9: "LR_ERR_INVALID_ARGUMENT", 10: "LR_ERR_WORKSPACE",
 }
 LR_OK = 0
 globals().update({v: k for k, v in STATUS.items()})
@@ -61,16 +61,23 @@ class LrPlan(ctypes.Structure):
         ("lds_bytes", ctypes.c_int32),
         ("reductions", ctypes.c_int32),
         ("row_aligned", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("splits", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
-        d = {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        d = {name: getattr(self, name) for name, _ in self._fields_}
         d["family"] = FAMILY_NAMES.get(self.family, self.family)
         return d
 
     def __repr__(self) -> str:
         return "LrPlan(%s)" % ", ".join("%s=%s" % kv for kv in self.as_dict().items())
+
+
+TENSOR_FIELDS = ("x", "residual", "gamma", "beta", "labels", "y", "sum_out", "losses", "sums", "mins", "maxs")
+
+
+class LrTensors(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in TENSOR_FIELDS]
 
 
 class LrDeviceFacts(ctypes.Structure):
@@ -125,11 +132,16 @@ def _load():
         "lr_plan_enumerate": [PF, I32, I64, I64, I32, I32, PP, I32, ctypes.POINTER(I32)],
         "lr_plan_validate": [PF, I32, I64, I64, I32, I32, PP],
         "lr_coverage_check": [PP, I64, I64, I32, P],
+        "lr_run_f32": [I32, ctypes.POINTER(LrTensors), I64, I64, F32, I32, PP, P, ctypes.c_uint64, P],
+        "lr_workspace_query": [I32, I64, I64, I32, ctypes.POINTER(ctypes.c_uint64)],
+        "lr_plan_for_device_ws": [PF, I32, I64, I64, I32, I32, PP],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.lr_plan_workspace_bytes.argtypes = [PP, I64]
+    lib.lr_plan_workspace_bytes.restype = ctypes.c_uint64
     lib.lr_device_facts_mi355x.argtypes = [PF]
     lib.lr_device_facts_mi355x.restype = None
     lib.lr_status_string.argtypes = [ctypes.c_int]
@@ -171,19 +183,62 @@ def _op(o):
     return OPS[o] if isinstance(o, str) else int(o)
 
 
+def _nbytes(t, n):
+    if n is not None:
+        return int(n)
+    if t is None:
+        return 0
+    return t.numel() * t.element_size()
+
+
 # ---------------------------------------------------------------------------
 # entry points (same names as the C ABI); each returns the lr_status code
 # ---------------------------------------------------------------------------
 
 
-def lr_softmax_f32(x, y, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None) -> int:
+def lr_run_f32(op, rows, cols, eps=0.0, policy=LR_UNORDERED_TREE, plan=None, workspace=None,
+               workspace_bytes=None, stream=None, **tensors) -> int:
+    """lr_run_f32: ``tensors`` are the lr_tensors members by name (x, y,
+    gamma, ...).  ``workspace`` is a device tensor or address;
+    ``workspace_bytes`` defaults to the tensor's size."""
+    unknown = set(tensors) - set(TENSOR_FIELDS)
+    if unknown:
+        raise TypeError("unknown tensor arguments: %s" % sorted(unknown))
+    t = LrTensors(**{k: _ptr(v) for k, v in tensors.items()})
+    if workspace is not None and workspace_bytes is None and isinstance(workspace, int):
+        raise TypeError("workspace_bytes is required with a raw workspace address")
+    return lib.lr_run_f32(_op(op), ctypes.byref(t), rows, cols, eps, _policy(policy),
+                          None if plan is None else ctypes.byref(plan), _ptr(workspace),
+                          _nbytes(workspace, workspace_bytes), _stream(stream))
+
+
+def lr_workspace_query(op, rows, cols, policy=LR_UNORDERED_TREE) -> int:
+    n = ctypes.c_uint64(0)
+    st = lib.lr_workspace_query(_op(op), rows, cols, _policy(policy), ctypes.byref(n))
+    if st != LR_OK:
+        raise LrError(st, "lr_workspace_query")
+    return n.value
+
+
+def lr_plan_workspace_bytes(plan, rows) -> int:
+    return int(lib.lr_plan_workspace_bytes(None if plan is None else ctypes.byref(plan), rows))
+
+
+def lr_softmax_f32(x, y, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None, workspace=None,
+                   workspace_bytes=None) -> int:
+    if workspace is not None:
+        return lr_run_f32("softmax", rows, cols, 0.0, policy, plan, workspace, workspace_bytes, stream, x=x, y=y)
     if plan is None:
         return lib.lr_softmax_f32(_ptr(x), _ptr(y), rows, cols, _policy(policy), _stream(stream))
     return lib.lr_softmax_f32_with_plan(_ptr(x), _ptr(y), rows, cols, _policy(policy),
                                         ctypes.byref(plan), _stream(stream))
 
 
-def lr_rmsnorm_f32(x, gamma, y, rows, cols, eps, policy=LR_UNORDERED_TREE, stream=None, plan=None) -> int:
+def lr_rmsnorm_f32(x, gamma, y, rows, cols, eps, policy=LR_UNORDERED_TREE, stream=None, plan=None,
+                   workspace=None, workspace_bytes=None) -> int:
+    if workspace is not None:
+        return lr_run_f32("rmsnorm", rows, cols, eps, policy, plan, workspace, workspace_bytes, stream,
+                          x=x, gamma=gamma, y=y)
     if plan is None:
         return lib.lr_rmsnorm_f32(_ptr(x), _ptr(gamma), _ptr(y), rows, cols, eps, _policy(policy),
                                   _stream(stream))
@@ -191,8 +246,11 @@ def lr_rmsnorm_f32(x, gamma, y, rows, cols, eps, policy=LR_UNORDERED_TREE, strea
                                         ctypes.byref(plan), _stream(stream))
 
 
-def lr_layernorm_f32(x, gamma, beta, y, rows, cols, eps, policy=LR_UNORDERED_TREE, stream=None,
-                     plan=None) -> int:
+def lr_layernorm_f32(x, gamma, beta, y, rows, cols, eps, policy=LR_UNORDERED_TREE, stream=None, plan=None,
+                     workspace=None, workspace_bytes=None) -> int:
+    if workspace is not None:
+        return lr_run_f32("layernorm", rows, cols, eps, policy, plan, workspace, workspace_bytes, stream,
+                          x=x, gamma=gamma, beta=beta, y=y)
     if plan is None:
         return lib.lr_layernorm_f32(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, eps,
                                     _policy(policy), _stream(stream))
@@ -200,8 +258,11 @@ def lr_layernorm_f32(x, gamma, beta, y, rows, cols, eps, policy=LR_UNORDERED_TRE
                                           _policy(policy), ctypes.byref(plan), _stream(stream))
 
 
-def lr_cross_entropy_f32(logits, labels, losses, rows, cols, policy=LR_UNORDERED_TREE, stream=None,
-                         plan=None) -> int:
+def lr_cross_entropy_f32(logits, labels, losses, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None,
+                         workspace=None, workspace_bytes=None) -> int:
+    if workspace is not None:
+        return lr_run_f32("cross_entropy", rows, cols, 0.0, policy, plan, workspace, workspace_bytes, stream,
+                          x=logits, labels=labels, losses=losses)
     if plan is None:
         return lib.lr_cross_entropy_f32(_ptr(logits), _ptr(labels), _ptr(losses), rows, cols,
                                         _policy(policy), _stream(stream))
@@ -210,7 +271,10 @@ def lr_cross_entropy_f32(logits, labels, losses, rows, cols, policy=LR_UNORDERED
 
 
 def lr_add_layernorm_f32(x, residual, gamma, beta, y, sum_out, rows, cols, eps, policy=LR_UNORDERED_TREE,
-                         stream=None, plan=None) -> int:
+                         stream=None, plan=None, workspace=None, workspace_bytes=None) -> int:
+    if workspace is not None:
+        return lr_run_f32("add_layernorm", rows, cols, eps, policy, plan, workspace, workspace_bytes, stream,
+                          x=x, residual=residual, gamma=gamma, beta=beta, y=y, sum_out=sum_out)
     if plan is None:
         return lib.lr_add_layernorm_f32(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(sum_out),
                                         rows, cols, eps, _policy(policy), _stream(stream))
@@ -219,14 +283,22 @@ def lr_add_layernorm_f32(x, residual, gamma, beta, y, sum_out, rows, cols, eps, 
                                               ctypes.byref(plan), _stream(stream))
 
 
-def lr_row_sum_f32(x, sums, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None) -> int:
+def lr_row_sum_f32(x, sums, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None, workspace=None,
+                   workspace_bytes=None) -> int:
+    if workspace is not None:
+        return lr_run_f32("row_sum", rows, cols, 0.0, policy, plan, workspace, workspace_bytes, stream,
+                          x=x, sums=sums)
     if plan is None:
         return lib.lr_row_sum_f32(_ptr(x), _ptr(sums), rows, cols, _policy(policy), _stream(stream))
     return lib.lr_row_sum_f32_with_plan(_ptr(x), _ptr(sums), rows, cols, _policy(policy), ctypes.byref(plan),
                                         _stream(stream))
 
 
-def lr_row_minmax_f32(x, mins, maxs, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None) -> int:
+def lr_row_minmax_f32(x, mins, maxs, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None,
+                      workspace=None, workspace_bytes=None) -> int:
+    if workspace is not None:
+        return lr_run_f32("row_minmax", rows, cols, 0.0, policy, plan, workspace, workspace_bytes, stream,
+                          x=x, mins=mins, maxs=maxs)
     if plan is None:
         return lib.lr_row_minmax_f32(_ptr(x), _ptr(mins), _ptr(maxs), rows, cols, _policy(policy),
                                      _stream(stream))
@@ -262,6 +334,15 @@ def lr_plan_for_device(facts, op, rows, cols, policy=LR_UNORDERED_TREE, row_alig
                                 ctypes.byref(p))
     if st != LR_OK:
         raise LrError(st, "lr_plan_for_device")
+    return p
+
+
+def lr_plan_for_device_ws(facts, op, rows, cols, policy=LR_UNORDERED_TREE, row_aligned=1) -> LrPlan:
+    p = LrPlan()
+    st = lib.lr_plan_for_device_ws(ctypes.byref(facts), _op(op), rows, cols, _policy(policy), row_aligned,
+                                   ctypes.byref(p))
+    if st != LR_OK:
+        raise LrError(st, "lr_plan_for_device_ws")
     return p
 
 

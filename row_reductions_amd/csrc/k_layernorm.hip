@@ -1,11 +1,12 @@
-// Unordered-policy kernels of one operation: every CACHE chunk count and the
-// STREAM family, each for aligned and misaligned rows (lr_kernels.hpp).
-#include "lr_kernels.hpp"
+// Unordered-policy kernels of one operation: every CACHE chunk count, the
+// STREAM family and the SPLIT family, each for aligned and misaligned rows
+// (lr_kernels.hpp, lr_split.hpp).
+#include "lr_split.hpp"
 
 namespace lr {
 
 hipError_t launch_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s) {
-    return launch_op<kLayerNorm>(a, p, aligned, s);
+    return launch_unordered<kLayerNorm>(a, p, aligned, s);
 }
 
 }  // namespace lr

@@ -3,6 +3,7 @@
 // and the full contract are in include/lr.h.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -74,6 +75,8 @@ struct Call {
     float* sums = nullptr;            // row sum
     float* mins = nullptr;            // row minimum, optional
     float* maxs = nullptr;            // row maximum, optional
+    void* workspace = nullptr;        // split family partials (lr_run_f32)
+    uint64_t workspace_bytes = 0;
 };
 
 lr_status validate_call(const Call& c) {
@@ -129,6 +132,22 @@ lr_status validate_call(const Call& c) {
         if (c.sum_out != nullptr && (!output_ok(c.sum_out) || overlap(range_of(c.sum_out, tb), range_of(c.y, tb))))
             return LR_ERR_ALIASING;
     }
+    if (c.workspace == nullptr && c.workspace_bytes > 0) return LR_ERR_NULL_POINTER;
+    if (c.workspace != nullptr && c.workspace_bytes > 0 && c.rows > 0) {
+        if (!aligned16(c.workspace)) return LR_ERR_MISALIGNED;
+        if (c.workspace_bytes > (uint64_t)INT64_MAX) return LR_ERR_INVALID_ARGUMENT;
+        // the workspace overlaps no tensor of the call
+        const Range rw = range_of(c.workspace, (int64_t)c.workspace_bytes);
+        const int64_t vb = c.cols * 4, ob = c.rows * 4;
+        const struct {
+            const void* p;
+            int64_t bytes;
+        } all[] = {{c.x, tb},          {c.residual, tb}, {c.y, tb},    {c.sum_out, tb}, {c.gamma, vb},
+                   {c.beta, vb},       {c.labels, c.rows * 8},         {c.losses, ob},  {c.sums, ob},
+                   {c.mins, ob},       {c.maxs, ob}};
+        for (const auto& t : all)
+            if (t.p != nullptr && overlap(rw, range_of(t.p, t.bytes))) return LR_ERR_ALIASING;
+    }
     return LR_OK;
 }
 
@@ -142,6 +161,11 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     const bool aligned = rows_aligned && (per_row || (aligned16(c.y) && aligned16(c.gamma) && aligned16(c.beta) &&
                                                       aligned16(c.residual) && aligned16(c.sum_out)));
 
+    const bool have_ws = c.workspace != nullptr && c.workspace_bytes > 0;
+    if (forced != nullptr && forced->family == LR_FAMILY_SPLIT &&
+        (!have_ws || c.workspace_bytes < (uint64_t)plan_workspace_bytes(*forced, c.rows)))
+        return LR_ERR_WORKSPACE;
+
     lr_device_facts facts;
     st = current_facts(&facts);
     if (st != LR_OK) return st;
@@ -151,9 +175,18 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
         if (st != LR_OK) return st;
         plan = *forced;
     } else {
-        st = lr_plan_for_device(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
-                                rows_aligned ? 1 : 0, &plan);
-        if (st != LR_OK) return st;
+        st = LR_ERR_INVALID_ARGUMENT;
+        if (have_ws) {
+            st = lr_plan_for_device_ws(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
+                                       rows_aligned ? 1 : 0, &plan);
+            if (st == LR_OK && c.workspace_bytes < (uint64_t)plan_workspace_bytes(plan, c.rows))
+                st = LR_ERR_WORKSPACE;  // too small to split: run unsplit
+        }
+        if (st != LR_OK) {
+            st = lr_plan_for_device(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
+                                    rows_aligned ? 1 : 0, &plan);
+            if (st != LR_OK) return st;
+        }
     }
 
     KArgs a;
@@ -183,6 +216,8 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     a.sum_out = c.sum_out;
     a.r_same_phase = same_phase(c.residual);
     a.s_same_phase = same_phase(c.sum_out);
+    a.splits = plan.family == LR_FAMILY_SPLIT ? plan.splits : 0;
+    a.ws = plan.family == LR_FAMILY_SPLIT ? static_cast<float*>(c.workspace) : nullptr;
 
     (void)hipGetLastError();  // clear a stale error so the launch's own status is seen
     hipError_t e;
@@ -330,6 +365,48 @@ lr_status lr_row_minmax_f32_with_plan(const float* x, float* mins, float* maxs, 
     return lr::run(c, plan, stream);
 }
 
+lr_status lr_run_f32(lr_op op, const lr_tensors* t, int64_t rows, int64_t cols, float eps,
+                     lr_reduction_policy policy, const lr_plan* plan, void* workspace, uint64_t workspace_bytes,
+                     hipStream_t stream) {
+    if (t == nullptr) return LR_ERR_NULL_POINTER;
+    if (op < LR_OP_SOFTMAX || op > LR_OP_ROW_MINMAX) return LR_ERR_INVALID_ARGUMENT;
+    // members the operation does not use must be NULL
+    const bool norm = op == LR_OP_RMSNORM || op == LR_OP_LAYERNORM || op == LR_OP_ADD_LAYERNORM;
+    const bool ln = op == LR_OP_LAYERNORM || op == LR_OP_ADD_LAYERNORM;
+    const bool dense_out = op == LR_OP_SOFTMAX || norm;
+    if ((t->residual && op != LR_OP_ADD_LAYERNORM) || (t->gamma && !norm) || (t->beta && !ln) ||
+        (t->labels && op != LR_OP_CROSS_ENTROPY) || (t->y && !dense_out) ||
+        (t->sum_out && op != LR_OP_ADD_LAYERNORM) || (t->losses && op != LR_OP_CROSS_ENTROPY) ||
+        (t->sums && op != LR_OP_ROW_SUM) || ((t->mins || t->maxs) && op != LR_OP_ROW_MINMAX))
+        return LR_ERR_INVALID_ARGUMENT;
+    Call c{op, t->x, t->gamma, t->beta, t->y, t->labels, t->losses, rows, cols, norm ? eps : 0.0f, policy};
+    c.residual = t->residual;
+    c.sum_out = t->sum_out;
+    c.sums = t->sums;
+    c.mins = t->mins;
+    c.maxs = t->maxs;
+    c.workspace = workspace;
+    c.workspace_bytes = workspace_bytes;
+    return lr::run(c, plan, stream);
+}
+
+lr_status lr_workspace_query(lr_op op, int64_t rows, int64_t cols, lr_reduction_policy policy, uint64_t* bytes) {
+    if (bytes == nullptr) return LR_ERR_NULL_POINTER;
+    lr_device_facts f;
+    lr_status st = lr::current_facts(&f);
+    if (st != LR_OK) return st;
+    // an aligned and a misaligned problem may plan differently: the larger need
+    uint64_t need = 0;
+    for (int32_t aligned = 0; aligned <= 1; ++aligned) {
+        lr_plan p;
+        st = lr_plan_for_device_ws(&f, op, rows, cols, policy, aligned, &p);
+        if (st != LR_OK) return st;
+        need = std::max(need, (uint64_t)lr::plan_workspace_bytes(p, rows));
+    }
+    *bytes = need;
+    return LR_OK;
+}
+
 lr_status lr_device_facts_query(lr_device_facts* out) {
     if (out == nullptr) return LR_ERR_NULL_POINTER;
     return lr::current_facts(out);
@@ -355,6 +432,7 @@ const char* lr_status_string(lr_status s) {
         case LR_ERR_UNREALIZABLE_PLAN: return "LR_ERR_UNREALIZABLE_PLAN: plan cannot be realised as given";
         case LR_ERR_HIP: return "LR_ERR_HIP: the HIP runtime reported an error";
         case LR_ERR_INVALID_ARGUMENT: return "LR_ERR_INVALID_ARGUMENT: invalid argument";
+        case LR_ERR_WORKSPACE: return "LR_ERR_WORKSPACE: the plan needs a larger workspace";
         default: return "unknown lr_status";
     }
 }

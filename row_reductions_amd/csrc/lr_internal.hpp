@@ -32,12 +32,17 @@ struct KArgs {
     float* sums;            // row sum: one float per row
     float* mins;            // row minimum (or null)
     float* maxs;            // row maximum (or null)
+    int32_t splits;         // split family: segments per row (G), else 0
+    float* ws;              // split family: 2 floats per segment, rows*G*2 floats
 };
 
 // Compiled cache-family chunk counts (chunks_per_lane), ascending.
 constexpr int kCacheChunks[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
 constexpr int kNumCacheChunks = sizeof(kCacheChunks) / sizeof(kCacheChunks[0]);
 constexpr int kStreamUnroll = 4;
+// Split-family chunk counts (the stripe of one segment), ascending.
+constexpr int kSplitChunks[] = {1, 2, 3, 4, 6, 8};
+constexpr int kNumSplitChunks = sizeof(kSplitChunks) / sizeof(kSplitChunks[0]);
 
 // Largest workgroup a cache instance is compiled for (launch bounds); the
 // register stripe grows with the chunk count, so the bound shrinks.
@@ -45,7 +50,10 @@ constexpr int cache_max_threads(int nch) { return nch <= 8 ? 1024 : (nch <= 16 ?
 
 bool cache_chunks_compiled(int nch);
 
-// Per-op launchers (one translation unit per op).  `aligned` selects the
+// Workspace bytes a plan needs for `rows` rows (0 unless it splits rows).
+int64_t plan_workspace_bytes(const lr_plan& p, int64_t rows);
+
+// Per-op launchers (one translation unit per op; CACHE, STREAM and SPLIT).  `aligned` selects the
 // instance for 16-byte aligned rows and parameter vectors.
 hipError_t launch_softmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_rmsnorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);

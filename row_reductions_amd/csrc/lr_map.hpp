@@ -27,6 +27,7 @@ constexpr int kVec = 4;         // floats per 128-bit chunk
 constexpr int kMaxWaves = 16;   // 1024 threads per workgroup
 constexpr int kSlab = 256;      // ordered family: floats folded per LDS slab
 constexpr int kTreeStack = 32;  // ordered family, tree policy: subtrees kept per wave (2^32 slabs)
+constexpr int kMaxSplits = 64;  // split family: segments per row (one wave lane per partial)
 
 // Ordered reduction policies (the lr_reduction_policy codes).
 enum Policy : int { kPolUnordered = 0, kPolFoldLeft = 1, kPolTree = 2, kPolFoldRight = 3 };
@@ -73,6 +74,20 @@ LR_HD bool elem_valid(int e, int cols) { return (unsigned)e < (unsigned)cols; }
 // Chunk k holds four row elements (no guard needed for it).
 LR_HD bool chunk_full(int k, int phase, int cols) {
     return kVec * k - phase >= 0 && kVec * k + kVec - phase <= cols;
+}
+
+// Split family: a row's nv chunks are cut into G segments of L = ceil(nv/G)
+// chunks; segment g holds chunks [k0, k1) (the last ones may be short or
+// empty).  Worker w of the segment's workgroup owns chunks k0 + w + W*c.
+struct SegmentBounds {
+    int k0, k1;
+};
+
+LR_HD SegmentBounds segment_bounds(int nv, int G, int g) {
+    const int L = (nv + G - 1) / G;
+    const int k0 = g * L < nv ? g * L : nv;
+    const int k1 = k0 + L < nv ? k0 + L : nv;
+    return SegmentBounds{k0, k1};
 }
 
 // Ordered family: one wavefront per row; lane l loads element

@@ -25,9 +25,34 @@ bool cache_chunks_compiled(int nch) {
     return false;
 }
 
+static bool split_chunks_compiled(int nch) {
+    for (int i = 0; i < kNumSplitChunks; ++i)
+        if (kSplitChunks[i] == nch) return true;
+    return false;
+}
+
+static int smallest_split_instance(int64_t need) {
+    for (int i = 0; i < kNumSplitChunks; ++i)
+        if (kSplitChunks[i] >= need) return kSplitChunks[i];
+    return 0;
+}
+
+int64_t plan_workspace_bytes(const lr_plan& p, int64_t rows) {
+    return p.family == LR_FAMILY_SPLIT && rows > 0 ? rows * (int64_t)p.splits * 2 * (int64_t)sizeof(float) : 0;
+}
+
 // 16-byte chunks a worker must reach for the widest row of the problem.
 static int64_t max_row_chunks(int64_t cols, bool aligned) {
     return aligned ? cols / kVec : (cols + 3 + kVec - 1) / kVec;  // phase up to 3
+}
+
+// Fewest 16-byte chunks a row of the problem spans (phase 0).
+static int64_t min_row_chunks(int64_t cols) { return (cols + kVec - 1) / kVec; }
+
+// Chunks per lane a SPLIT plan needs: the longest segment over W = 64*S lanes.
+static int64_t split_need(int64_t cols, bool aligned, int G, int S) {
+    const int64_t L = (max_row_chunks(cols, aligned) + G - 1) / G;
+    return (L + kWave * S - 1) / (kWave * S);
 }
 
 static int reductions_of(int op) {
@@ -40,7 +65,8 @@ static int smallest_cache_instance(int64_t need) {
     return 0;
 }
 
-static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_t cols, int op, bool aligned) {
+static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_t cols, int op, bool aligned,
+                        int splits = 0) {
     lr_plan p;
     std::memset(&p, 0, sizeof(p));
     p.family = family;
@@ -49,7 +75,8 @@ static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_
     p.vec = family == LR_FAMILY_ORDERED ? 1 : kVec;
     p.chunks_per_lane = nch;
     p.threads_per_block = kWave * S * Q;
-    p.blocks = (rows + Q - 1) / Q;
+    p.splits = family == LR_FAMILY_SPLIT ? splits : 0;
+    p.blocks = family == LR_FAMILY_SPLIT ? rows * splits : (rows + Q - 1) / Q;
     p.reductions = reductions_of(op);
     p.lds_bytes = family == LR_FAMILY_ORDERED ? Q * (kSlab + kTreeStack) * 4
                   : family == LR_FAMILY_TREE  ? 2 * kMaxWaves * 4 + 2 * kMaxWaves * 128 * 4
@@ -61,11 +88,12 @@ static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_
 static bool valid_op(int op) { return op >= LR_OP_SOFTMAX && op <= LR_OP_ROW_MINMAX; }
 static bool valid_policy(int p) { return p >= LR_UNORDERED_TREE && p <= LR_FOLD_RIGHT; }
 
-// Families a policy may run on: unordered -> CACHE, STREAM; fold_left and
-// fold_right -> ORDERED; ordered_tree -> TREE, ORDERED.
+// Families a policy may run on: unordered -> CACHE, STREAM, SPLIT; fold_left
+// and fold_right -> ORDERED; ordered_tree -> TREE, ORDERED.
 static bool family_allowed(int policy, int family) {
     switch (policy) {
-        case LR_UNORDERED_TREE: return family == LR_FAMILY_CACHE || family == LR_FAMILY_STREAM;
+        case LR_UNORDERED_TREE:
+            return family == LR_FAMILY_CACHE || family == LR_FAMILY_STREAM || family == LR_FAMILY_SPLIT;
         case LR_ORDERED_TREE: return family == LR_FAMILY_TREE || family == LR_FAMILY_ORDERED;
         default: return family == LR_FAMILY_ORDERED;
     }
@@ -90,9 +118,19 @@ lr_status validate_plan(const lr_device_facts* f, int op, int64_t rows, int64_t 
     if (S < 1 || Q < 1 || S > kMaxWaves || Q > kMaxWaves || S * Q > kMaxWaves) return LR_ERR_UNREALIZABLE_PLAN;
     if (p->threads_per_block != kWave * S * Q || p->threads_per_block > f->max_threads_per_block)
         return LR_ERR_UNREALIZABLE_PLAN;
-    const int64_t blocks = (rows + Q - 1) / Q;
-    if (p->blocks != blocks || blocks > INT32_MAX) return LR_ERR_UNREALIZABLE_PLAN;
     if (!family_allowed(policy, p->family)) return LR_ERR_UNREALIZABLE_PLAN;
+    if (p->family == LR_FAMILY_SPLIT) {
+        // one segment per workgroup; every lane of a merging wave holds one
+        // partial, and no row has fewer chunks than segments
+        const int G = p->splits;
+        if (Q != 1 || G < 2 || G > kMaxSplits || G > min_row_chunks(cols)) return LR_ERR_UNREALIZABLE_PLAN;
+        if (p->blocks != rows * G || p->blocks > INT32_MAX) return LR_ERR_UNREALIZABLE_PLAN;
+        if (p->vec != kVec || !split_chunks_compiled(p->chunks_per_lane)) return LR_ERR_UNREALIZABLE_PLAN;
+        if (p->chunks_per_lane < split_need(cols, aligned, G, S)) return LR_ERR_UNREALIZABLE_PLAN;
+        return LR_OK;
+    }
+    const int64_t blocks = (rows + Q - 1) / Q;
+    if (p->splits != 0 || p->blocks != blocks || blocks > INT32_MAX) return LR_ERR_UNREALIZABLE_PLAN;
     switch (p->family) {
         case LR_FAMILY_TREE:
             // the cache layout with aligned rows; at most 128 slabs of 256 floats
@@ -147,6 +185,11 @@ static int enumerate_all(const lr_device_facts* f, int op, int64_t rows, int64_t
     for (int S = 1; S <= kMaxWaves; ++S)
         for (int Q = 1; S * Q <= kMaxWaves; ++Q)
             push(make_plan(LR_FAMILY_STREAM, S, Q, kStreamUnroll, rows, cols, op, aligned));
+    for (int G = 2; G <= kMaxSplits && G <= min_row_chunks(cols); G *= 2)
+        for (int S = 1; S <= kMaxWaves; ++S) {
+            const int nch = smallest_split_instance(split_need(cols, aligned, G, S));
+            if (nch != 0) push(make_plan(LR_FAMILY_SPLIT, S, 1, nch, rows, cols, op, aligned, G));
+        }
     return n;
 }
 
@@ -172,20 +215,70 @@ struct TableEntry {
     int64_t cols;
     int aligned;
     int family, S, Q, nch;
+    int splits;  // SPLIT entries only
 };
 
 static const TableEntry kTable[] = {
 #include "lr_plan_table.inc"
 };
 
+// Rows too few to fill the device, when a workspace is available: G
+// segments per row, G the smallest power of two with rows*G >= the CU count,
+// halved while a segment would hold fewer than 256 chunks (1024 floats: the
+// second launch has to pay for itself); S the fewest waves with a stripe of
+// at most 4 chunks per lane.  G < 2 means: do not split.  Only the LayerNorms
+// split: on MI355X at 64 x 12289 their one-launch kernels take 10-12 us (two
+// statistics passes, then the gamma and beta reads), which a second launch
+// beats (8-9.4 us); softmax, RMSNorm, cross-entropy and the row sum finish
+// in 4-7 us in one launch, faster than any split plan.
+static lr_plan split_prior(const lr_device_facts* f, int op, int64_t rows, int64_t cols, bool aligned) {
+    lr_plan none;
+    std::memset(&none, 0, sizeof(none));
+    const int64_t cus = f->compute_units;
+    if (op != LR_OP_LAYERNORM && op != LR_OP_ADD_LAYERNORM) return none;
+    if (rows < 1 || 2 * rows > cus) return none;
+    int G = 1;
+    while (G < kMaxSplits && rows * G < cus) G *= 2;
+    while (G >= 2 && min_row_chunks(cols) / G < 256) G /= 2;
+    if (G < 2) return none;
+    int S = 1;
+    while (S < kMaxWaves && split_need(cols, aligned, G, S) > 4) ++S;
+    const int nch = smallest_split_instance(split_need(cols, aligned, G, S));
+    if (nch == 0) return none;
+    return make_plan(LR_FAMILY_SPLIT, S, 1, nch, rows, cols, op, aligned, G);
+}
+
 static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy,
-                          bool aligned) {
-    for (const TableEntry& e : kTable) {
-        if (e.op == op && e.policy == policy && e.rows == rows && e.cols == cols &&
-            e.aligned == (aligned ? 1 : 0)) {
-            lr_plan p = make_plan(e.family, e.S, e.Q, e.nch, rows, cols, op, aligned);
+                          bool aligned, bool allow_split) {
+    auto matches = [&](const TableEntry& e) {
+        return e.op == op && e.policy == policy && e.rows == rows && e.cols == cols && e.aligned == (aligned ? 1 : 0);
+    };
+    auto from_entry = [&](const TableEntry& e) {
+        return make_plan(e.family, e.S, e.Q, e.nch, rows, cols, op, aligned, e.splits);
+    };
+    if (allow_split && policy == LR_UNORDERED_TREE) {
+        // a measured SPLIT winner; else the split prior, unless a measured
+        // workspace-free winner is listed for the shape
+        bool listed = false;
+        for (const TableEntry& e : kTable) {
+            if (!matches(e)) continue;
+            if (e.family != LR_FAMILY_SPLIT) {
+                listed = true;
+                continue;
+            }
+            lr_plan p = from_entry(e);
             if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
         }
+        if (!listed) {
+            lr_plan p = split_prior(f, op, rows, cols, aligned);
+            if (p.family == LR_FAMILY_SPLIT && validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK)
+                return p;
+        }
+    }
+    for (const TableEntry& e : kTable) {
+        if (!matches(e) || e.family == LR_FAMILY_SPLIT) continue;
+        lr_plan p = from_entry(e);
+        if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
     }
     const int64_t simds = (int64_t)f->compute_units * (f->simds_per_cu > 0 ? f->simds_per_cu : 4);
     const int64_t nv = max_row_chunks(cols, aligned);
@@ -235,11 +328,28 @@ extern "C" lr_status lr_plan_for_device(const lr_device_facts* facts, lr_op op, 
     if (st != LR_OK) return st;
     if (out == nullptr) return LR_ERR_NULL_POINTER;
     const bool aligned = row_aligned != 0 && cols % kVec == 0;
-    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned);
+    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned, false);
     st = validate_plan(facts, op, rows, cols, policy, aligned, &p);
     if (st != LR_OK) return st;
     *out = p;
     return LR_OK;
+}
+
+extern "C" lr_status lr_plan_for_device_ws(const lr_device_facts* facts, lr_op op, int64_t rows, int64_t cols,
+                                           lr_reduction_policy policy, int32_t row_aligned, lr_plan* out) {
+    lr_status st = check_problem(facts, op, rows, cols, policy);
+    if (st != LR_OK) return st;
+    if (out == nullptr) return LR_ERR_NULL_POINTER;
+    const bool aligned = row_aligned != 0 && cols % kVec == 0;
+    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned, true);
+    st = validate_plan(facts, op, rows, cols, policy, aligned, &p);
+    if (st != LR_OK) return st;
+    *out = p;
+    return LR_OK;
+}
+
+extern "C" uint64_t lr_plan_workspace_bytes(const lr_plan* plan, int64_t rows) {
+    return plan == nullptr ? 0 : (uint64_t)plan_workspace_bytes(*plan, rows);
 }
 
 extern "C" lr_status lr_plan_enumerate(const lr_device_facts* facts, lr_op op, int64_t rows, int64_t cols,
@@ -267,8 +377,28 @@ extern "C" lr_status lr_coverage_check(const lr_plan* p, int64_t rows, int64_t c
     const int S = p->waves_per_row, Q = p->rows_per_block;
     if (S < 1 || Q < 1 || p->threads_per_block != kWave * S * Q) return LR_ERR_UNREALIZABLE_PLAN;
     const int c = (int)cols;
+    if (p->family == LR_FAMILY_SPLIT && (p->splits < 1 || Q != 1)) return LR_ERR_UNREALIZABLE_PLAN;
     for (int64_t b = 0; b < p->blocks; ++b) {
         for (int tid = 0; tid < p->threads_per_block; ++tid) {
+            if (p->family == LR_FAMILY_SPLIT) {
+                // block b holds segment b % G of row b / G (workers w + W*i)
+                const Team t = team_of(tid, S);
+                const int W = kWave * S;
+                const int64_t row = b / p->splits;
+                if (row >= rows) continue;
+                const int h = (int)((phase + (row * cols) % kVec) % kVec);
+                const int nv = chunks_of(h, c);
+                const SegmentBounds sb = segment_bounds(nv, p->splits, (int)(b % p->splits));
+                for (int i = 0; i < p->chunks_per_lane; ++i) {
+                    const int k = sb.k0 + chunk_index(t.w, W, i);
+                    if (k >= sb.k1) continue;
+                    for (int j = 0; j < kVec; ++j) {
+                        const int e = elem_index(k, j, h);
+                        if (elem_valid(e, c)) counts[row * cols + e] += 1;
+                    }
+                }
+                continue;
+            }
             if (p->family == LR_FAMILY_ORDERED) {
                 const int lane = tid % kWave, wave = tid / kWave;
                 const int64_t row = row_of(b, Q, wave);

@@ -24,24 +24,27 @@ import torch
 import row_reductions_amd as lr
 
 
-def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh, rs=None, ys2=None):
+def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh, rs=None, ys2=None, ws=None):
+    """run(i, plan): one launch on buffer set i; split plans use workspace ws."""
     pol = lr._policy(policy)
 
     def run(i, plan):
         k = i % len(xs)
+        w = ws if plan is not None and plan.family == lr.LR_FAMILY_SPLIT else None
         if op == "softmax":
-            return lr.lr_softmax_f32(xs[k], ys[k], rows, cols, pol, sh, plan)
+            return lr.lr_softmax_f32(xs[k], ys[k], rows, cols, pol, sh, plan, workspace=w)
         if op == "rmsnorm":
-            return lr.lr_rmsnorm_f32(xs[k], g, ys[k], rows, cols, eps, pol, sh, plan)
+            return lr.lr_rmsnorm_f32(xs[k], g, ys[k], rows, cols, eps, pol, sh, plan, workspace=w)
         if op == "layernorm":
-            return lr.lr_layernorm_f32(xs[k], g, b, ys[k], rows, cols, eps, pol, sh, plan)
+            return lr.lr_layernorm_f32(xs[k], g, b, ys[k], rows, cols, eps, pol, sh, plan, workspace=w)
         if op == "add_layernorm":
-            return lr.lr_add_layernorm_f32(xs[k], rs[k], g, b, ys[k], None, rows, cols, eps, pol, sh, plan)
+            return lr.lr_add_layernorm_f32(xs[k], rs[k], g, b, ys[k], None, rows, cols, eps, pol, sh, plan,
+                                           workspace=w)
         if op == "row_sum":
-            return lr.lr_row_sum_f32(xs[k], ys[k], rows, cols, pol, sh, plan)
+            return lr.lr_row_sum_f32(xs[k], ys[k], rows, cols, pol, sh, plan, workspace=w)
         if op == "row_minmax":
-            return lr.lr_row_minmax_f32(xs[k], ys[k], ys2[k], rows, cols, pol, sh, plan)
-        return lr.lr_cross_entropy_f32(xs[k], lab, ys[k], rows, cols, pol, sh, plan)
+            return lr.lr_row_minmax_f32(xs[k], ys[k], ys2[k], rows, cols, pol, sh, plan, workspace=w)
+        return lr.lr_cross_entropy_f32(xs[k], lab, ys[k], rows, cols, pol, sh, plan, workspace=w)
     return run
 
 
@@ -93,7 +96,8 @@ def main(argv=None):
     b = torch.randn(cols, device=dev, generator=gen) * 0.1
     lab = torch.randint(0, cols, (rows,), device=dev, generator=gen)
     rs = [torch.randn(rows, cols, device=dev, generator=gen) for _ in range(sets)] if op == "add_layernorm" else None
-    run = _launcher(op, xs, ys, g, b, lab, rows, cols, args.eps, args.policy, sh, rs, ys2)
+    ws = torch.empty(rows * 64 * 8, dtype=torch.uint8, device=dev)  # the largest split: 64 segments
+    run = _launcher(op, xs, ys, g, b, lab, rows, cols, args.eps, args.policy, sh, rs, ys2, ws)
 
     facts = lr.lr_device_facts_query()
     aligned = 1 if cols % 4 == 0 else 0
@@ -125,13 +129,24 @@ def main(argv=None):
           f"best {again:.2f} us ({moved / again / 1e3:.0f} GB/s): {best!r}")
     for us, p, rec in results[:8]:
         print(f"#   {us:8.2f} us  {p!r}")
-    fam = {0: "LR_FAMILY_CACHE", 1: "LR_FAMILY_STREAM", 2: "LR_FAMILY_ORDERED", 3: "LR_FAMILY_TREE"}[best.family]
+    fam = {0: "LR_FAMILY_CACHE", 1: "LR_FAMILY_STREAM", 2: "LR_FAMILY_ORDERED", 3: "LR_FAMILY_TREE",
+           4: "LR_FAMILY_SPLIT"}
     opn = {0: "LR_OP_SOFTMAX", 1: "LR_OP_RMSNORM", 2: "LR_OP_LAYERNORM", 3: "LR_OP_CROSS_ENTROPY",
            4: "LR_OP_ADD_LAYERNORM", 5: "LR_OP_ROW_SUM", 6: "LR_OP_ROW_MINMAX"}[lr.OPS[op]]
     pol = {"unordered_tree": "LR_UNORDERED_TREE", "ordered_fold": "LR_ORDERED_FOLD", "fold_left": "LR_ORDERED_FOLD",
            "ordered_tree": "LR_ORDERED_TREE", "fold_right": "LR_FOLD_RIGHT"}[args.policy]
-    print(f"{{{opn}, {pol}, {rows}, {cols}, {aligned}, {fam}, {best.waves_per_row}, "
-          f"{best.rows_per_block}, {best.chunks_per_lane}}},")
+
+    def table_line(p):
+        tail = f", {p.splits}" if p.family == lr.LR_FAMILY_SPLIT else ""
+        return (f"{{{opn}, {pol}, {rows}, {cols}, {aligned}, {fam[p.family]}, {p.waves_per_row}, "
+                f"{p.rows_per_block}, {p.chunks_per_lane}{tail}}},")
+    # the best plan, and the best that needs no workspace (the typed entry
+    # points' choice) when the best splits rows
+    print(table_line(best))
+    if best.family == lr.LR_FAMILY_SPLIT:
+        free = next(t for t in results if t[1].family != lr.LR_FAMILY_SPLIT)
+        print(f"# best without a workspace: {free[0]:.2f} us")
+        print(table_line(free[1]))
     return 0
 
 

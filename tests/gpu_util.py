@@ -28,17 +28,28 @@ def dev(a: np.ndarray | None, pad: int = 0):
     return view.view(t.shape), full
 
 
+def workspace_for(plan, rows):
+    """A workspace for a split-family plan (None for any other), filled with
+    NaN bytes: the call must overwrite every partial it reads."""
+    n = lr.lr_plan_workspace_bytes(plan, rows) if plan is not None else 0
+    if n == 0:
+        return None
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)
+
+
 def run_gpu(op: str, inp: dict, eps=None, policy="unordered_tree", plan=None, x_pad=0, y_pad=0,
-            canary=None, in_place=False):
-    """Runs `op` on the GPU and returns (output as numpy, status, extras)."""
+            canary=None, in_place=False, workspace=None):
+    """Runs `op` on the GPU and returns (output as numpy, status, extras).
+    A split-family plan gets a workspace of its own unless one is given."""
     x = inp["logits"] if op == "cross_entropy" else inp["x"]
     rows, cols = x.shape
     xv = dev(x, x_pad)[0] if x_pad else dev(x)
     extras = {}
+    ws = workspace if workspace is not None else workspace_for(plan, rows)
     if op == "cross_entropy":
         lab = dev(inp["labels"])
         out = torch.empty(rows, dtype=torch.float32, device=DEV)
-        st = lr.lr_cross_entropy_f32(xv, lab, out, rows, cols, policy, plan=plan)
+        st = lr.lr_cross_entropy_f32(xv, lab, out, rows, cols, policy, plan=plan, workspace=ws)
     else:
         if in_place:
             yv, yfull = xv, None
@@ -51,12 +62,12 @@ def run_gpu(op: str, inp: dict, eps=None, policy="unordered_tree", plan=None, x_
             yfull = None
             yv = torch.empty(rows, cols, dtype=torch.float32, device=DEV)
         if op == "softmax":
-            st = lr.lr_softmax_f32(xv, yv, rows, cols, policy, plan=plan)
+            st = lr.lr_softmax_f32(xv, yv, rows, cols, policy, plan=plan, workspace=ws)
         elif op == "rmsnorm":
-            st = lr.lr_rmsnorm_f32(xv, dev(inp.get("gamma")), yv, rows, cols, eps, policy, plan=plan)
+            st = lr.lr_rmsnorm_f32(xv, dev(inp.get("gamma")), yv, rows, cols, eps, policy, plan=plan, workspace=ws)
         else:
             st = lr.lr_layernorm_f32(xv, dev(inp.get("gamma")), dev(inp.get("beta")), yv, rows, cols, eps,
-                                     policy, plan=plan)
+                                     policy, plan=plan, workspace=ws)
         out = yv
         extras["yfull"] = yfull
     torch.cuda.synchronize()

@@ -2,6 +2,7 @@
 include/lr.h declares, and rejects bad arguments with the documented status
 before making any HIP call (no GPU is needed for any check here)."""
 import ctypes
+import functools
 import os
 import re
 
@@ -123,3 +124,60 @@ def test_valid_call_without_device_reports_hip_error():
     assert lr.lr_add_layernorm_f32(X, X, None, None, Y, None, 4, 8, 1e-5, 0, 0) == lr.LR_ERR_HIP
     assert lr.lr_row_sum_f32(X, LOSS, 4, 8, 1, 0) == lr.LR_ERR_HIP
     assert lr.lr_row_minmax_f32(X, None, LOSS, 4, 8, 0, 0) == lr.LR_ERR_HIP
+
+
+WS = 0x7F0080000000
+RUN = functools.partial(lr.lr_run_f32, stream=0)  # no torch stream on a CPU host
+
+
+def _split_plan(rows, cols, G=4, S=4, nch=3):
+    p = lr.LrPlan()
+    p.family, p.waves_per_row, p.rows_per_block, p.vec = lr.LR_FAMILY_SPLIT, S, 1, 4
+    p.chunks_per_lane, p.threads_per_block, p.blocks, p.splits = nch, 64 * S, rows * G, G
+    p.row_aligned = 1
+    return p
+
+
+@pytest.mark.parametrize("call,status", [
+    (lambda: lr.lib.lr_run_f32(0, None, 4, 8, 0.0, 0, None, None, 0, None), lr.LR_ERR_NULL_POINTER),
+    (lambda: RUN("softmax", 4, 8, x=X, y=Y, gamma=G), lr.LR_ERR_INVALID_ARGUMENT),
+    (lambda: RUN("rmsnorm", 4, 8, 1e-6, x=X, y=Y, beta=B), lr.LR_ERR_INVALID_ARGUMENT),
+    (lambda: RUN("row_sum", 4, 8, x=X, sums=LOSS, mins=SUM), lr.LR_ERR_INVALID_ARGUMENT),
+    (lambda: RUN("cross_entropy", 4, 8, x=X, labels=LAB, losses=LOSS, y=Y), lr.LR_ERR_INVALID_ARGUMENT),
+    (lambda: RUN(7, 4, 8, x=X, y=Y), lr.LR_ERR_INVALID_ARGUMENT),
+    (lambda: RUN("softmax", 4, 8, x=X), lr.LR_ERR_NULL_POINTER),
+    # workspace: NULL with a size, misaligned, overlapping a tensor of the call
+    (lambda: RUN("softmax", 4, 8, workspace=0, workspace_bytes=64, x=X, y=Y), lr.LR_ERR_NULL_POINTER),
+    (lambda: RUN("softmax", 4, 8, workspace=WS + 8, workspace_bytes=64, x=X, y=Y), lr.LR_ERR_MISALIGNED),
+    (lambda: RUN("softmax", 4, 8, workspace=X + 64, workspace_bytes=64, x=X, y=Y), lr.LR_ERR_ALIASING),
+    (lambda: RUN("layernorm", 4, 8, 1e-5, workspace=G + 16, workspace_bytes=64, x=X, y=Y, gamma=G),
+     lr.LR_ERR_ALIASING),
+    (lambda: RUN("cross_entropy", 4, 8, workspace=LAB - 16, workspace_bytes=32, x=X, labels=LAB,
+                           losses=LOSS), lr.LR_ERR_ALIASING),
+    (lambda: RUN("row_minmax", 4, 8, workspace=SUM, workspace_bytes=64, x=X, maxs=SUM + 32),
+     lr.LR_ERR_ALIASING),
+    # a split plan without the workspace it needs: rows * splits * 8 bytes
+    (lambda: lr.lr_layernorm_f32(X, G, B, Y, 64, 12288, 1e-5, 0, plan=_split_plan(64, 12288), stream=0),
+     lr.LR_ERR_WORKSPACE),
+    (lambda: RUN("layernorm", 64, 12288, 1e-5, plan=_split_plan(64, 12288), workspace=WS,
+                 workspace_bytes=64 * 4 * 8 - 1, x=X, y=Y), lr.LR_ERR_WORKSPACE),
+    (lambda: lr.lr_row_sum_f32(X, LOSS, 64, 12288, 0, plan=_split_plan(64, 12288), stream=0), lr.LR_ERR_WORKSPACE),
+    # the run call validates like the typed ones
+    (lambda: RUN("rmsnorm", 4, 8, float("nan"), x=X, y=Y), lr.LR_ERR_INVALID_EPS),
+    (lambda: RUN("softmax", 4, 8, policy=9, x=X, y=Y), lr.LR_ERR_INVALID_POLICY),
+    (lambda: RUN("softmax", 4, 8, x=X, y=X + 4), lr.LR_ERR_ALIASING),
+])
+def test_run_and_workspace_validation_before_any_hip_call(call, status):
+    assert call() == status
+
+
+def test_run_without_device_reports_hip_error():
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is present")
+    assert RUN("softmax", 0, 8, x=X, y=Y) == lr.LR_OK  # nothing to launch
+    assert RUN("softmax", 4, 8, x=X, y=Y) == lr.LR_ERR_HIP
+    ws = dict(workspace=WS, workspace_bytes=64 * 4 * 8)
+    assert RUN("layernorm", 64, 12288, 1e-5, plan=_split_plan(64, 12288), x=X, y=Y, **ws) == lr.LR_ERR_HIP
+    assert lr.lr_softmax_f32(X, Y, 64, 12288, stream=0, workspace=WS, workspace_bytes=1 << 20) == lr.LR_ERR_HIP
+    with pytest.raises(lr.LrError):
+        lr.lr_workspace_query("layernorm", 64, 12289)

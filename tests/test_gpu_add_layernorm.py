@@ -13,7 +13,7 @@ import torch
 import oracle
 import row_reductions_amd as lr
 import synth
-from gpu_util import DEV, assert_parity, dev
+from gpu_util import DEV, assert_parity, dev, workspace_for
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,8 @@ def run_add(inp, policy="unordered_tree", plan=None, with_sum=True, affine=True,
             sv = place(None, pads[3])
     g = dev(inp["gamma"]) if affine else None
     b = dev(inp["beta"]) if affine else None
-    st = lr.lr_add_layernorm_f32(xv, rv, g, b, yv, sv, rows, cols, EPS, policy, plan=plan)
+    st = lr.lr_add_layernorm_f32(xv, rv, g, b, yv, sv, rows, cols, EPS, policy, plan=plan,
+                                 workspace=workspace_for(plan, rows))
     torch.cuda.synchronize()
     return st, yv.cpu().numpy(), (sv.cpu().numpy() if sv is not None else None)
 

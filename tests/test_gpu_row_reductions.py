@@ -17,7 +17,7 @@ import torch
 import oracle
 import row_reductions_amd as lr
 import synth
-from gpu_util import DEV
+from gpu_util import DEV, workspace_for
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def gpu_sum(x, policy, plan=None, pad=0):
     rows, cols = x.shape
     xv = place(x, pad)
     out = torch.full((rows,), float("nan"), device=DEV)
-    st = lr.lr_row_sum_f32(xv, out, rows, cols, policy, plan=plan)
+    st = lr.lr_row_sum_f32(xv, out, rows, cols, policy, plan=plan, workspace=workspace_for(plan, rows))
     torch.cuda.synchronize()
     return st, out.cpu().numpy()
 
@@ -44,7 +44,7 @@ def gpu_minmax(x, policy, plan=None, pad=0, want=(True, True)):
     xv = place(x, pad)
     lo = torch.full((rows,), float("nan"), device=DEV) if want[0] else None
     hi = torch.full((rows,), float("nan"), device=DEV) if want[1] else None
-    st = lr.lr_row_minmax_f32(xv, lo, hi, rows, cols, policy, plan=plan)
+    st = lr.lr_row_minmax_f32(xv, lo, hi, rows, cols, policy, plan=plan, workspace=workspace_for(plan, rows))
     torch.cuda.synchronize()
     return st, (lo.cpu().numpy() if lo is not None else None), (hi.cpu().numpy() if hi is not None else None)
 

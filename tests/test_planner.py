@@ -58,9 +58,18 @@ def test_plans_respect_device_limits():
             for policy in POLICIES:
                 for p in lr.lr_plan_enumerate(F, op, rows, cols, policy, 1 if cols % 4 == 0 else 0):
                     assert p.threads_per_block == 64 * p.waves_per_row * p.rows_per_block <= 1024
-                    assert p.blocks == -(-rows // p.rows_per_block)
+                    if p.family == lr.LR_FAMILY_SPLIT:
+                        assert p.rows_per_block == 1 and 2 <= p.splits <= 64
+                        assert p.blocks == rows * p.splits
+                        seg = -(-((cols + 6) // 4 if cols % 4 else cols // 4) // p.splits)
+                        assert p.chunks_per_lane in (1, 2, 3, 4, 6, 8)
+                        assert p.chunks_per_lane * 64 * p.waves_per_row >= seg
+                        assert lr.lr_plan_workspace_bytes(p, rows) == rows * p.splits * 8
+                    else:
+                        assert p.splits == 0 and lr.lr_plan_workspace_bytes(p, rows) == 0
+                        assert p.blocks == -(-rows // p.rows_per_block)
                     assert p.lds_bytes <= 64 * 1024
-                    if p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_TREE):
+                    if p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_TREE) and p.splits == 0:
                         need = -(-((cols + 6) // 4 if cols % 4 else cols // 4) // (64 * p.waves_per_row))
                         assert p.chunks_per_lane >= need
                         assert p.chunks_per_lane in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32)
@@ -71,7 +80,7 @@ def test_plans_respect_device_limits():
                         if p.family == lr.LR_FAMILY_TREE:
                             assert cols % 4 == 0 and cols <= 32768
                     if policy == "unordered_tree":
-                        assert p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_STREAM)
+                        assert p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_STREAM, lr.LR_FAMILY_SPLIT)
 
 
 def test_automatic_plan_is_legal_and_deterministic():
@@ -84,6 +93,12 @@ def test_automatic_plan_is_legal_and_deterministic():
                 b = lr.lr_plan_for_device(F, op, rows, cols, policy, al)
                 assert bytes(a) == bytes(b)
                 assert lr.lr_plan_validate(F, op, rows, cols, policy, al, a) == lr.LR_OK
+                assert a.family != lr.LR_FAMILY_SPLIT  # the typed calls have no workspace
+                w = lr.lr_plan_for_device_ws(F, op, rows, cols, policy, al)
+                assert bytes(w) == bytes(lr.lr_plan_for_device_ws(F, op, rows, cols, policy, al))
+                assert lr.lr_plan_validate(F, op, rows, cols, policy, al, w) == lr.LR_OK
+                if w.family != lr.LR_FAMILY_SPLIT:
+                    assert bytes(w) == bytes(a)
 
 
 def _plan(**kw):
@@ -153,3 +168,76 @@ def test_planner_argument_errors():
     n = ctypes.c_int32(-1)
     assert lr.lib.lr_plan_enumerate(ctypes.byref(F), 0, 4, 4, 0, 1, None, 0, ctypes.byref(n)) == lr.LR_OK
     assert n.value > 0
+
+
+def _split(rows, cols, G, S, nch, aligned=1):
+    p = lr.LrPlan()
+    p.family, p.waves_per_row, p.rows_per_block, p.vec = lr.LR_FAMILY_SPLIT, S, 1, 4
+    p.chunks_per_lane, p.threads_per_block, p.blocks, p.splits = nch, 64 * S, rows * G, G
+    p.lds_bytes, p.reductions, p.row_aligned = 128, 2, aligned
+    return p
+
+
+def test_split_plan_legality():
+    ok = _split(64, 12288, 4, 4, 3)  # 3072 chunks: 768 per segment over 256 lanes
+    assert lr.lr_plan_validate(F, "layernorm", 64, 12288, "unordered_tree", 1, ok) == lr.LR_OK
+    # the same stripe is one chunk short for misaligned rows (3073 chunks)
+    assert lr.lr_plan_validate(F, "layernorm", 64, 12288, "unordered_tree", 0, ok) == lr.LR_ERR_UNREALIZABLE_PLAN
+    bad = [
+        dict(splits=1, blocks=64), dict(splits=65, blocks=64 * 65), dict(blocks=65),
+        dict(chunks_per_lane=5), dict(chunks_per_lane=12), dict(chunks_per_lane=2),
+        dict(rows_per_block=2, threads_per_block=512), dict(vec=1),
+    ]
+    for change in bad:
+        p = _split(64, 12288, 4, 4, 3)
+        for k, v in change.items():
+            setattr(p, k, v)
+        assert lr.lr_plan_validate(F, "layernorm", 64, 12288, "unordered_tree", 1, p) == \
+            lr.LR_ERR_UNREALIZABLE_PLAN, change
+    # no segment without a chunk of its own: splits <= the row's chunk count
+    assert lr.lr_plan_validate(F, "softmax", 3, 20, "unordered_tree", 1, _split(3, 20, 5, 1, 1)) == lr.LR_OK
+    assert lr.lr_plan_validate(F, "softmax", 3, 20, "unordered_tree", 1, _split(3, 20, 6, 1, 1)) == \
+        lr.LR_ERR_UNREALIZABLE_PLAN
+    # only the unordered policy splits rows, and other families carry no splits
+    for pol in ("ordered_fold", "ordered_tree", "fold_right"):
+        assert lr.lr_plan_validate(F, "layernorm", 64, 12288, pol, 1, ok) == lr.LR_ERR_UNREALIZABLE_PLAN
+    c = lr.lr_plan_for_device(F, "layernorm", 64, 12288, "unordered_tree", 1)
+    c.splits = 2
+    assert lr.lr_plan_validate(F, "layernorm", 64, 12288, "unordered_tree", 1, c) == lr.LR_ERR_UNREALIZABLE_PLAN
+
+
+def test_workspace_plan_splits_few_long_rows_only():
+    for op in OPS:
+        w = lr.lr_plan_for_device_ws(F, op, 64, 12289, "unordered_tree", 0)
+        if op in ("layernorm", "add_layernorm"):
+            assert w.family == lr.LR_FAMILY_SPLIT and w.splits >= 2 and w.blocks >= 256, (op, w)
+            assert lr.lr_plan_workspace_bytes(w, 64) == 64 * w.splits * 8
+            # the prior too (no measured entry at 48 rows)
+            v = lr.lr_plan_for_device_ws(F, op, 48, 16384, "unordered_tree", 1)
+            assert v.family == lr.LR_FAMILY_SPLIT and v.blocks >= 256, (op, v)
+        else:  # one launch is faster for these
+            assert w.family != lr.LR_FAMILY_SPLIT, (op, w)
+        # enough rows to fill the device, or rows too short to be worth a
+        # second launch: no split
+        for rows, cols in [(768, 6144), (4096, 32000), (37, 1537), (64, 512)]:
+            v = lr.lr_plan_for_device_ws(F, op, rows, cols, "unordered_tree", 1 if cols % 4 == 0 else 0)
+            assert v.family != lr.LR_FAMILY_SPLIT, (op, rows, cols, v)
+        for pol in ("ordered_fold", "ordered_tree", "fold_right"):
+            assert lr.lr_plan_for_device_ws(F, op, 64, 12289, pol, 0).family != lr.LR_FAMILY_SPLIT
+    assert lr.lr_plan_workspace_bytes(None, 64) == 0
+
+
+def test_split_plans_cover_each_element_once_including_empty_segments():
+    # 20 floats = 5 chunks in 4 segments of 2: the last segment is empty on
+    # aligned rows; misaligned rows span 6 chunks
+    for rows, cols, G in [(3, 20, 4), (2, 21, 4), (5, 130, 32), (2, 12289, 4), (3, 1537, 16), (1, 4096, 64)]:
+        for S in (1, 2, 3):
+            aligned = 1 if cols % 4 == 0 else 0
+            need = -(-(-(-((cols + 6) // 4 if not aligned else cols // 4) // G)) // (64 * S))
+            nch = next(n for n in (1, 2, 3, 4, 6, 8, 99) if n >= need)
+            if nch == 99:
+                continue
+            p = _split(rows, cols, G, S, nch, aligned)
+            assert lr.lr_plan_validate(F, "softmax", rows, cols, "unordered_tree", aligned, p) == lr.LR_OK
+            for ph in ((0,) if aligned else (0, 1, 2, 3)):
+                assert (coverage(p, rows, cols, ph) == 1).all(), (rows, cols, G, S, ph)
