@@ -43,11 +43,15 @@ PAGES_M1MAX_STEP_US = 57.414 + 60.753 + 75.251
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_768x6144.json")
 
 
-def traffic_bytes(op: str):
+def traffic_bytes(lr, op: str):
     """HBM bytes per launch of `op` from the committed FETCH_SIZE / WRITE_SIZE
-    summary (copy-calibrated), or None when the kernels changed since."""
+    summary (copy-calibrated), or None when the kernels changed since or the
+    summary was taken for another kernel instance than this plan's."""
     from row_reductions_amd import profiling
-    rec = profiling.lookup(TRAFFIC_SUMMARY, op)
+    plan = lr.lr_plan_query(op, ROWS, COLS, "unordered_tree")
+    params = {"softmax": 0, "rmsnorm": 1, "layernorm": 1}[op]  # gamma (and beta) present
+    kernel = profiling.kernel_name(lr.OPS[op], plan, True, params)
+    rec = profiling.lookup(TRAFFIC_SUMMARY, op, kernel)
     return None if rec is None else round(rec["traffic_bytes"])
 
 
@@ -227,7 +231,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_bytes(dominant),
+            "traffic": traffic_bytes(lr, dominant),
             "bytes_per_launch": b,
             "avg_launch_us": round(per_op_us[dominant], 3),
         },

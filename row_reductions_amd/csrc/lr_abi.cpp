@@ -175,14 +175,17 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
         if (st != LR_OK) return st;
         plan = *forced;
     } else {
-        st = LR_ERR_INVALID_ARGUMENT;
+        // with a workspace large enough, the plan that may split rows;
+        // otherwise the typed entry points' plan
+        bool split_ok = false;
         if (have_ws) {
-            st = lr_plan_for_device_ws(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
-                                       rows_aligned ? 1 : 0, &plan);
-            if (st == LR_OK && c.workspace_bytes < (uint64_t)plan_workspace_bytes(plan, c.rows))
-                st = LR_ERR_WORKSPACE;  // too small to split: run unsplit
+            lr_plan w;
+            split_ok = lr_plan_for_device_ws(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
+                                             rows_aligned ? 1 : 0, &w) == LR_OK &&
+                       c.workspace_bytes >= (uint64_t)plan_workspace_bytes(w, c.rows);
+            if (split_ok) plan = w;
         }
-        if (st != LR_OK) {
+        if (!split_ok) {
             st = lr_plan_for_device(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
                                     rows_aligned ? 1 : 0, &plan);
             if (st != LR_OK) return st;

@@ -5,8 +5,10 @@ WRITE_SIZE, both launched with `bench.py --copy-probe`) give KiB per
 dispatch for every kernel.  The counters are calibrated against a plain
 device-to-device copy of known size that runs in the same process (the last
 20 `__amd_rocclr_copyBuffer` dispatches): bytes = counter * (known bytes /
-copy's counter).  The summary records a hash of the HIP sources, so a figure
-taken before a kernel change is not reported for the changed kernel.
+copy's counter).  The summary records a hash of the device sources (the
+`.hip` translation units and the headers they compile), so a figure taken
+before a kernel change is not reported for the changed kernel; a lookup also
+names the exact kernel instance the caller's plan launches.
 
     python -m row_reductions_amd.profiling traffic --fetch F.csv --write W.csv \\
         --copy-bytes 18874368 --out profiles/hbm_traffic_768x6144.json
@@ -27,10 +29,12 @@ OP_NAMES = {0: "softmax", 1: "rmsnorm", 2: "layernorm", 3: "cross_entropy"}
 
 
 def csrc_hash() -> str:
-    """sha256 over the library's HIP/C++ sources (names and contents)."""
+    """sha256 over the device sources: the `.hip` translation units and the
+    `.hpp` headers (names and contents).  Host-only files (the C ABI, the
+    planner and its table) do not change a kernel."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".inc", ".h")):
+        if name.endswith((".hip", ".hpp")):
             h.update(name.encode())
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())
@@ -84,8 +88,20 @@ def traffic(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
     return out
 
 
-def lookup(summary_path: str, op: str):
-    """Traffic record of `op` if the summary matches the current sources."""
+def kernel_name(op_index: int, plan, aligned: bool, param_mode: int) -> str | None:
+    """The demangled name of the kernel instance a CACHE or STREAM plan
+    launches (param_mode: 0 no gamma/beta, 1 all present, 2 some)."""
+    al = "true" if aligned else "false"
+    if plan.family == 0:
+        return f"void lr::k_cache<{op_index}, {plan.chunks_per_lane}, {al}, {param_mode}>(lr::KArgs)"
+    if plan.family == 1:
+        return f"void lr::k_stream<{op_index}, {al}>(lr::KArgs)"
+    return None
+
+
+def lookup(summary_path: str, op: str, kernel: str | None = None):
+    """Traffic record of `op` if the summary matches the current device
+    sources and, when `kernel` is given, was taken for that kernel."""
     try:
         with open(summary_path) as f:
             s = json.load(f)
@@ -94,7 +110,7 @@ def lookup(summary_path: str, op: str):
     if s.get("csrc_sha256") != csrc_hash():
         return None
     for name, rec in s.get("kernels", {}).items():
-        if rec.get("op") == op:
+        if rec.get("op") == op and (kernel is None or name == kernel):
             return dict(rec, kernel=name)
     return None
 

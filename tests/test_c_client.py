@@ -2,8 +2,9 @@
 the HIP runtime header, is compiled by gcc as C11 and links liblr.so.  On the
 CPU the client must compile and link; on the GPU it must run its checks
 (softmax rows sum to one under every policy, RMSNorm of constant rows,
-cross-entropy of uniform rows with an out-of-range label, and argument
-errors returned before any device work)."""
+cross-entropy of uniform rows with an out-of-range label, a LayerNorm split
+across workgroups through lr_run_f32 and a workspace, and argument errors
+returned before any device work)."""
 import os
 import shutil
 import subprocess
