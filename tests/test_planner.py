@@ -241,3 +241,26 @@ def test_split_plans_cover_each_element_once_including_empty_segments():
             assert lr.lr_plan_validate(F, "softmax", rows, cols, "unordered_tree", aligned, p) == lr.LR_OK
             for ph in ((0,) if aligned else (0, 1, 2, 3)):
                 assert (coverage(p, rows, cols, ph) == 1).all(), (rows, cols, G, S, ph)
+
+
+def test_planner_is_thread_safe():
+    """the pure planner from many host threads at once gives the plans one
+    thread gives (ctypes releases the GIL during each call)"""
+    import threading
+    shapes = [(r, c) for r in (1, 37, 64, 256, 768, 4096) for c in (1, 257, 1537, 6144, 12289, 32000)]
+    want = {(op, r, c): bytes(lr.lr_plan_for_device_ws(F, op, r, c, "unordered_tree", 0))
+            for op in OPS for r, c in shapes}
+    bad = []
+
+    def worker():
+        for _ in range(5):
+            for (op, r, c), b in want.items():
+                if bytes(lr.lr_plan_for_device_ws(F, op, r, c, "unordered_tree", 0)) != b:
+                    bad.append((op, r, c))
+
+    ts = [threading.Thread(target=worker) for _ in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not bad
