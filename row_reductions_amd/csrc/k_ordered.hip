@@ -51,10 +51,28 @@ __device__ __forceinline__ float contrib(float x, float ref) {
     return expf(x - ref);  // kExpShift: ref is the row maximum
 }
 
-// Element j of the row: x_j, or the FP32 sum x_j + residual_j when the row
-// is the fused residual LayerNorm's combined input (rr not null).
-__device__ __forceinline__ float row_elem(const float* xr, const float* rr, int e) {
-    return rr ? xr[e] + rr[e] : xr[e];
+// Elementwise passes (the row's maximum, minimum, and the output) walk the
+// row in trips of kPass elements per lane, element base + 64*u + lane at slot
+// u, through buffer resources: every load of a trip is issued before the
+// first is used, and a load past the row returns 0 (a store past it is
+// dropped).  An element loop that used each load at once would wait for one
+// memory round trip per element.
+constexpr int kPass = 8;
+
+__device__ __forceinline__ int pass_elem(int base, int u, int lane) { return base + kWave * u + lane; }
+
+// The row's maximum, exact in any order (the wave tree combines the lanes).
+__device__ __forceinline__ float row_max(BufRes rx, int cols, int lane) {
+    float m = -INFINITY;
+    for (int base = 0; base < cols; base += kWave * kPass) {
+        float v[kPass];
+#pragma unroll
+        for (int u = 0; u < kPass; ++u) v[u] = res_ld1(rx, pass_elem(base, u, lane) * 4);
+#pragma unroll
+        for (int u = 0; u < kPass; ++u)
+            if (pass_elem(base, u, lane) < cols) m = fmaxf(m, v[u]);
+    }
+    return wave_allreduce<MaxOp>(m);
 }
 
 // Folds one full 256-entry slab into acc, left to right (FOLD_RIGHT: right to
@@ -190,10 +208,9 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
     float* stk = stacks[wave];
     const float n = (float)cols;
 
+    const BufRes rx = make_res(xr, cols * 4);
     if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
-        float m = -INFINITY;
-        for (int e = lane; e < cols; e += kWave) m = fmaxf(m, xr[e]);
-        m = wave_allreduce<MaxOp>(m);
+        const float m = row_max(rx, cols, lane);
         const float s = ordered_sum<kExpShift, POL>(xr, nullptr, cols, m, slab, stk, lane);
         if constexpr (OP == kCrossEntropy) {
             if (lane == 0) {
@@ -202,8 +219,14 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
                 a.losses[row] = (logf(s) + m) - sel;
             }
         } else {
-            float* yr = a.y + row * (int64_t)cols;
-            for (int e = lane; e < cols; e += kWave) yr[e] = expf(xr[e] - m) / s;
+            const BufRes ry = make_res(a.y + row * (int64_t)cols, cols * 4);
+            for (int base = 0; base < cols; base += kWave * kPass) {
+                float v[kPass];
+#pragma unroll
+                for (int u = 0; u < kPass; ++u) v[u] = res_ld1(rx, pass_elem(base, u, lane) * 4);
+#pragma unroll
+                for (int u = 0; u < kPass; ++u) res_st1(ry, pass_elem(base, u, lane) * 4, expf(v[u] - m) / s);
+            }
         }
     } else if constexpr (OP == kRowSum) {
         const float sum = ordered_sum<kValue, POL>(xr, nullptr, cols, 0.0f, slab, stk, lane);
@@ -211,9 +234,17 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
     } else if constexpr (OP == kRowMinMax) {
         // exact in any order: the wave tree, as the max fold above
         float lo = INFINITY, hi = -INFINITY;
-        for (int e = lane; e < cols; e += kWave) {
-            lo = fmin2(lo, xr[e]);
-            hi = fmax2(hi, xr[e]);
+        for (int base = 0; base < cols; base += kWave * kPass) {
+            float v[kPass];
+#pragma unroll
+            for (int u = 0; u < kPass; ++u) v[u] = res_ld1(rx, pass_elem(base, u, lane) * 4);
+#pragma unroll
+            for (int u = 0; u < kPass; ++u) {
+                if (pass_elem(base, u, lane) < cols) {
+                    lo = fmin2(lo, v[u]);
+                    hi = fmax2(hi, v[u]);
+                }
+            }
         }
         lo = wave_allreduce<MinOp>(lo);
         hi = wave_allreduce<MaxOp>(hi);
@@ -225,27 +256,53 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
         const float ss = ordered_sum<kSquare, POL>(xr, nullptr, cols, 0.0f, slab, stk, lane);
         const float ms = ss / n;
         const float r = 1.0f / sqrtf(ms + a.eps);
-        float* yr = a.y + row * (int64_t)cols;
-        for (int e = lane; e < cols; e += kWave) {
-            const float t = xr[e] * r;
-            yr[e] = a.gamma ? t * a.gamma[e] : t;
+        const BufRes ry = make_res(a.y + row * (int64_t)cols, cols * 4);
+        const BufRes rg = make_res(a.gamma, a.gamma ? cols * 4 : 0);
+        for (int base = 0; base < cols; base += kWave * kPass) {
+            float v[kPass], g[kPass];
+#pragma unroll
+            for (int u = 0; u < kPass; ++u) {
+                v[u] = res_ld1(rx, pass_elem(base, u, lane) * 4);
+                g[u] = res_ld1(rg, pass_elem(base, u, lane) * 4);
+            }
+#pragma unroll
+            for (int u = 0; u < kPass; ++u) {
+                const float t = v[u] * r;
+                res_st1(ry, pass_elem(base, u, lane) * 4, a.gamma ? t * g[u] : t);
+            }
         }
     } else {  // LayerNorm; fused residual LayerNorm folds over x + residual
         const float* rr = OP == kAddLayerNorm ? a.residual + row * (int64_t)cols : nullptr;
         const float mu = ordered_sum<kValue, POL>(xr, rr, cols, 0.0f, slab, stk, lane) / n;
         const float var = ordered_sum<kCentredSquare, POL>(xr, rr, cols, mu, slab, stk, lane) / n;
         const float r = 1.0f / sqrtf(var + a.eps);
-        float* yr = a.y + row * (int64_t)cols;
-        float* sr = (OP == kAddLayerNorm && a.sum_out) ? a.sum_out + row * (int64_t)cols : nullptr;
-        for (int e = lane; e < cols; e += kWave) {
-            // every read of element e precedes its writes (y or the sum may be
-            // x or the residual itself)
-            const float c = row_elem(xr, rr, e);
-            float t = (c - mu) * r;
-            if (a.gamma) t = t * a.gamma[e];
-            if (a.beta) t = t + a.beta[e];
-            yr[e] = t;
-            if (sr) sr[e] = c;
+        const BufRes ry = make_res(a.y + row * (int64_t)cols, cols * 4);
+        const bool with_sum = OP == kAddLayerNorm && a.sum_out != nullptr;
+        const BufRes rs = make_res(with_sum ? a.sum_out + row * (int64_t)cols : nullptr, with_sum ? cols * 4 : 0);
+        const BufRes rres = make_res(rr, rr ? cols * 4 : 0);
+        const BufRes rg = make_res(a.gamma, a.gamma ? cols * 4 : 0);
+        const BufRes rb = make_res(a.beta, a.beta ? cols * 4 : 0);
+        for (int base = 0; base < cols; base += kWave * kPass) {
+            // every read of a trip's elements precedes their writes (y or the
+            // sum may be x or the residual itself)
+            float c[kPass], g[kPass], b[kPass];
+#pragma unroll
+            for (int u = 0; u < kPass; ++u) {
+                const int off = pass_elem(base, u, lane) * 4;
+                c[u] = res_ld1(rx, off);
+                if (rr) c[u] = c[u] + res_ld1(rres, off);
+                g[u] = res_ld1(rg, off);
+                b[u] = res_ld1(rb, off);
+            }
+#pragma unroll
+            for (int u = 0; u < kPass; ++u) {
+                const int off = pass_elem(base, u, lane) * 4;
+                float t = (c[u] - mu) * r;
+                if (a.gamma) t = t * g[u];
+                if (a.beta) t = t + b[u];
+                res_st1(ry, off, t);
+                if (with_sum) res_st1(rs, off, c[u]);
+            }
         }
     }
 }

@@ -175,6 +175,11 @@ __device__ __forceinline__ float res_ld1(BufRes r, int byte_off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kAuxDefault));
 }
 
+__device__ __forceinline__ void res_st1(BufRes r, int byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, byte_off, 0,
+                                          LR_NT_STORES ? kAuxNt : kAuxDefault);
+}
+
 __device__ __forceinline__ void res_st4(BufRes r, int byte_off, float4 v) {
     const v4f w = {v.x, v.y, v.z, v.w};
     __builtin_amdgcn_raw_buffer_store_b128(w, r, byte_off, 0, LR_NT_STORES ? kAuxNt : kAuxDefault);
