@@ -211,4 +211,31 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 
 __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// Softmax state over a row team with one exchange: every wave brings its
+// own (max m_w, sum of exp(x - m_w)) pair, lane 0 publishes it, one workgroup
+// barrier, then every wave merges the S pairs ("TIRx Metal reduction
+// lowering", section 1, the online softmax state): M = max_w m_w,
+// s = sum_w s_w exp(m_w - M).  A wave with no element of the row brings
+// (-inf, 0).  `sm`, `ss`: this round's LDS arrays of Q*S floats.
+struct MaxSum {
+    float m, s;
+};
+
+__device__ __forceinline__ MaxSum team_maxsum(float m, float s, float* sm, float* ss, int S, const Team& t) {
+    if (S > 1) {
+        if (t.lane == 0) {
+            sm[t.q * S + t.s] = m;
+            ss[t.q * S + t.s] = s;
+        }
+        __syncthreads();
+        const bool in = t.lane < S;
+        const float mi = in ? sm[t.q * S + t.lane] : -INFINITY;
+        const float si = in ? ss[t.q * S + t.lane] : 0.0f;
+        const float M = wave_allreduce<MaxOp>(mi);
+        const float sc = (mi == -INFINITY) ? 0.0f : si * fast_exp(mi - M);
+        return MaxSum{M, wave_allreduce<AddOp>(sc)};
+    }
+    return MaxSum{m, s};
+}
+
 }  // namespace lr
