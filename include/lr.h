@@ -24,9 +24,11 @@
  *           output may be exactly its input tensor (y == x: in place).  Any
  *           other overlap returns LR_ERR_ALIASING (the pages' kernel ABI is
  *           noalias, section 3).
- * Shapes.   rows >= 0, cols >= 1, rows*cols*4 must fit in int64, cols < 2^24
- *           (so that cols is exact in FP32).  rows == 0 returns LR_OK and
- *           launches nothing.
+ * Shapes.   0 <= rows <= INT32_MAX, cols >= 1, rows*cols*4 must fit in
+ *           int64, cols < 2^24 (so that cols is exact in FP32); else
+ *           LR_ERR_INVALID_SHAPE.  rows == 0 returns LR_OK and launches
+ *           nothing.  A call whose grid would pass one dispatch's reach runs
+ *           as several dispatches in order on `stream` (lr_dispatch_rows).
  * Streams.  Work is enqueued on `stream` (NULL = the default stream) and the
  *           call returns without synchronising.  A launch failure reported
  *           by the HIP runtime returns LR_ERR_HIP.
@@ -322,6 +324,14 @@ lr_status lr_workspace_query(lr_op op, int64_t rows, int64_t cols, lr_reduction_
 /* Workspace bytes `plan` needs for `rows` rows: rows * splits * 8 for a SPLIT
  * plan, 0 for any other (and for a NULL plan). */
 uint64_t lr_plan_workspace_bytes(const lr_plan* plan, int64_t rows);
+
+/* Rows one kernel dispatch of `plan` covers in a call over `rows` rows.  A
+ * dispatch carries at most 2^31 work-items (the dispatch packet's grid size
+ * is 32 bits), so a call whose grid would be larger -- only possible with
+ * about 2^21 rows or more -- runs as consecutive dispatches of this many rows
+ * on its stream, the last one holding the rest; results are those of one
+ * dispatch.  Returns 0 for a NULL plan or rows < 1. */
+int64_t lr_dispatch_rows(const lr_plan* plan, int64_t rows);
 
 /* ---------------------------------------------------------------------------
  * Planner (host only; no device memory touched)

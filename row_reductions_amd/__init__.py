@@ -9,7 +9,7 @@ torch stream, an integer ``hipStream_t`` handle, or None for the current
 torch stream.
 
 Importing this package raises ImportError when liblr.so has not been built
-(``python -m row_reductions_amd.build``): there is no fallback path.
+(``python row_reductions_amd/build.py``): there is no fallback path.
 """
 from __future__ import annotations
 
@@ -106,7 +106,7 @@ def _load():
         pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m row_reductions_amd.build` (no CPU fallback exists)")
+            f"{LIB_PATH} is not built; run `python row_reductions_amd/build.py` (no CPU fallback exists)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     PP = ctypes.POINTER(LrPlan)
@@ -142,6 +142,8 @@ def _load():
         fn.restype = ctypes.c_int
     lib.lr_plan_workspace_bytes.argtypes = [PP, I64]
     lib.lr_plan_workspace_bytes.restype = ctypes.c_uint64
+    lib.lr_dispatch_rows.argtypes = [PP, I64]
+    lib.lr_dispatch_rows.restype = I64
     lib.lr_device_facts_mi355x.argtypes = [PF]
     lib.lr_device_facts_mi355x.restype = None
     lib.lr_status_string.argtypes = [ctypes.c_int]
@@ -222,6 +224,10 @@ def lr_workspace_query(op, rows, cols, policy=LR_UNORDERED_TREE) -> int:
 
 def lr_plan_workspace_bytes(plan, rows) -> int:
     return int(lib.lr_plan_workspace_bytes(None if plan is None else ctypes.byref(plan), rows))
+
+
+def lr_dispatch_rows(plan, rows) -> int:
+    return int(lib.lr_dispatch_rows(None if plan is None else ctypes.byref(plan), rows))
 
 
 def lr_softmax_f32(x, y, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None, workspace=None,

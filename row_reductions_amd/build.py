@@ -1,6 +1,9 @@
 """Builds liblr.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-    python -m row_reductions_amd.build
+    python row_reductions_amd/build.py
+
+(run as a script: it does not import the package, whose import loads the
+library it is about to replace).
 
 Objects go to ``_build/`` at the repository root; the shared library is
 written next to this file, where the Python binding loads it.

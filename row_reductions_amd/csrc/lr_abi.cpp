@@ -151,6 +151,52 @@ lr_status validate_call(const Call& c) {
     return LR_OK;
 }
 
+hipError_t launch_piece(int op, int policy, const KArgs& a, const lr_plan& plan, bool aligned, hipStream_t stream) {
+    if (plan.family == LR_FAMILY_ORDERED) return launch_ordered(op, policy, a, plan, stream);
+    if (plan.family == LR_FAMILY_TREE) {
+        switch (op) {
+            case LR_OP_SOFTMAX: return launch_tree_softmax(a, plan, aligned, stream);
+            case LR_OP_RMSNORM: return launch_tree_rmsnorm(a, plan, aligned, stream);
+            case LR_OP_LAYERNORM: return launch_tree_layernorm(a, plan, aligned, stream);
+            case LR_OP_ADD_LAYERNORM: return launch_tree_add_layernorm(a, plan, aligned, stream);
+            case LR_OP_ROW_SUM: return launch_tree_row_sum(a, plan, aligned, stream);
+            case LR_OP_ROW_MINMAX: return launch_tree_row_minmax(a, plan, aligned, stream);
+            default: return launch_tree_cross_entropy(a, plan, aligned, stream);
+        }
+    }
+    switch (op) {
+        case LR_OP_SOFTMAX: return launch_softmax(a, plan, aligned, stream);
+        case LR_OP_RMSNORM: return launch_rmsnorm(a, plan, aligned, stream);
+        case LR_OP_LAYERNORM: return launch_layernorm(a, plan, aligned, stream);
+        case LR_OP_ADD_LAYERNORM: return launch_add_layernorm(a, plan, aligned, stream);
+        case LR_OP_ROW_SUM: return launch_row_sum(a, plan, aligned, stream);
+        case LR_OP_ROW_MINMAX: return launch_row_minmax(a, plan, aligned, stream);
+        default: return launch_cross_entropy(a, plan, aligned, stream);
+    }
+}
+
+// Arguments of the row piece [r0, r0 + n): every row pointer advanced by r0
+// rows.  A row's 16-byte phase is read from its own address and the
+// same-phase flags compare two row pointers advanced alike, so both carry
+// over.  The split workspace is not advanced: pieces run one after another on
+// one stream and each needs no more of it than the whole call.
+KArgs piece_args(const KArgs& a, int64_t r0, int64_t n, bool per_row) {
+    auto adv = [](auto* p, int64_t k) { return p == nullptr ? p : p + k; };
+    const int64_t e0 = r0 * a.cols;
+    KArgs b = a;
+    b.rows = n;
+    b.x = adv(a.x, e0);
+    b.y = per_row ? a.y : adv(a.y, e0);
+    b.residual = adv(a.residual, e0);
+    b.sum_out = adv(a.sum_out, e0);
+    b.labels = adv(a.labels, r0);
+    b.losses = adv(a.losses, r0);
+    b.sums = adv(a.sums, r0);
+    b.mins = adv(a.mins, r0);
+    b.maxs = adv(a.maxs, r0);
+    return b;
+}
+
 lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     lr_status st = validate_call(c);
     if (st != LR_OK) return st;
@@ -223,31 +269,15 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
     a.ws = plan.family == LR_FAMILY_SPLIT ? static_cast<float*>(c.workspace) : nullptr;
 
     (void)hipGetLastError();  // clear a stale error so the launch's own status is seen
-    hipError_t e;
-    if (plan.family == LR_FAMILY_ORDERED) {
-        e = launch_ordered(c.op, c.policy, a, plan, stream);
-    } else if (plan.family == LR_FAMILY_TREE) {
-        switch (c.op) {
-            case LR_OP_SOFTMAX: e = launch_tree_softmax(a, plan, aligned, stream); break;
-            case LR_OP_RMSNORM: e = launch_tree_rmsnorm(a, plan, aligned, stream); break;
-            case LR_OP_LAYERNORM: e = launch_tree_layernorm(a, plan, aligned, stream); break;
-            case LR_OP_ADD_LAYERNORM: e = launch_tree_add_layernorm(a, plan, aligned, stream); break;
-            case LR_OP_ROW_SUM: e = launch_tree_row_sum(a, plan, aligned, stream); break;
-            case LR_OP_ROW_MINMAX: e = launch_tree_row_minmax(a, plan, aligned, stream); break;
-            default: e = launch_tree_cross_entropy(a, plan, aligned, stream); break;
-        }
-    } else {
-        switch (c.op) {
-            case LR_OP_SOFTMAX: e = launch_softmax(a, plan, aligned, stream); break;
-            case LR_OP_RMSNORM: e = launch_rmsnorm(a, plan, aligned, stream); break;
-            case LR_OP_LAYERNORM: e = launch_layernorm(a, plan, aligned, stream); break;
-            case LR_OP_ADD_LAYERNORM: e = launch_add_layernorm(a, plan, aligned, stream); break;
-            case LR_OP_ROW_SUM: e = launch_row_sum(a, plan, aligned, stream); break;
-            case LR_OP_ROW_MINMAX: e = launch_row_minmax(a, plan, aligned, stream); break;
-            default: e = launch_cross_entropy(a, plan, aligned, stream); break;
-        }
+    // rows beyond one dispatch's reach run as consecutive pieces on `stream`
+    const int64_t step = dispatch_rows(plan, c.rows);
+    for (int64_t r0 = 0; r0 < c.rows; r0 += step) {
+        const int64_t n = std::min(step, c.rows - r0);
+        const hipError_t e = launch_piece(c.op, c.policy, piece_args(a, r0, n, per_row),
+                                          piece_plan(plan, n), aligned, stream);
+        if (e != hipSuccess) return LR_ERR_HIP;
     }
-    return e == hipSuccess ? LR_OK : LR_ERR_HIP;
+    return LR_OK;
 }
 
 }  // namespace

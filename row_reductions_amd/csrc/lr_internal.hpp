@@ -53,6 +53,19 @@ bool cache_chunks_compiled(int nch);
 // Workspace bytes a plan needs for `rows` rows (0 unless it splits rows).
 int64_t plan_workspace_bytes(const lr_plan& p, int64_t rows);
 
+// Work-items one kernel dispatch may carry.  The dispatch packet holds a
+// 32-bit grid size; staying at 2^31 also keeps blockIdx * blockDim inside a
+// signed 32-bit int.
+constexpr int64_t kMaxDispatchItems = int64_t(1) << 31;
+
+// Rows one dispatch of plan `p` covers for a call over `rows` rows (at least
+// 1, at most `rows`); a multiple of rows_per_block whenever it is below rows.
+int64_t dispatch_rows(const lr_plan& p, int64_t rows);
+
+// `p` resized to a piece of n rows (its grid: ceil(n / Q) workgroups, or
+// n * splits for the split family).
+lr_plan piece_plan(const lr_plan& p, int64_t n);
+
 // Per-op launchers (one translation unit per op; CACHE, STREAM and SPLIT).  `aligned` selects the
 // instance for 16-byte aligned rows and parameter vectors.
 hipError_t launch_softmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);

@@ -41,6 +41,19 @@ int64_t plan_workspace_bytes(const lr_plan& p, int64_t rows) {
     return p.family == LR_FAMILY_SPLIT && rows > 0 ? rows * (int64_t)p.splits * 2 * (int64_t)sizeof(float) : 0;
 }
 
+int64_t dispatch_rows(const lr_plan& p, int64_t rows) {
+    const int64_t blocks = kMaxDispatchItems / std::max<int64_t>(1, p.threads_per_block);
+    const int64_t per = p.family == LR_FAMILY_SPLIT ? blocks / std::max<int64_t>(1, p.splits)
+                                                    : blocks * std::max<int64_t>(1, p.rows_per_block);
+    return std::max<int64_t>(1, std::min(per, rows));
+}
+
+lr_plan piece_plan(const lr_plan& p, int64_t n) {
+    lr_plan q = p;
+    q.blocks = p.family == LR_FAMILY_SPLIT ? n * p.splits : (n + p.rows_per_block - 1) / p.rows_per_block;
+    return q;
+}
+
 // 16-byte chunks a worker must reach for the widest row of the problem.
 static int64_t max_row_chunks(int64_t cols, bool aligned) {
     return aligned ? cols / kVec : (cols + 3 + kVec - 1) / kVec;  // phase up to 3
@@ -350,6 +363,10 @@ extern "C" lr_status lr_plan_for_device_ws(const lr_device_facts* facts, lr_op o
 
 extern "C" uint64_t lr_plan_workspace_bytes(const lr_plan* plan, int64_t rows) {
     return plan == nullptr ? 0 : (uint64_t)plan_workspace_bytes(*plan, rows);
+}
+
+extern "C" int64_t lr_dispatch_rows(const lr_plan* plan, int64_t rows) {
+    return plan == nullptr || rows < 1 ? 0 : dispatch_rows(*plan, rows);
 }
 
 extern "C" lr_status lr_plan_enumerate(const lr_device_facts* facts, lr_op op, int64_t rows, int64_t cols,

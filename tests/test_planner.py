@@ -264,3 +264,40 @@ def test_planner_is_thread_safe():
     for t in ts:
         t.join()
     assert not bad
+
+
+def test_dispatch_rows_keep_each_dispatch_within_2_31_work_items():
+    """a call runs as dispatches of lr_dispatch_rows rows: each carries at most
+    2^31 work-items, pieces below the whole call hold whole workgroups of
+    rows, and problems of fewer than about 2^21 rows take one dispatch"""
+    limit = 1 << 31
+    checked = 0
+    for rows, cols in ((1, 1), (5, 3), (1 << 21, 1), ((1 << 26) + 3, 1), ((1 << 31) - 1, 1), (1 << 22, 2),
+                       (3 << 20, 6144), (64, 12289), (2, (1 << 24) - 1)):
+        for op in OPS:
+            for policy in POLICIES:
+                for aligned in ((1, 0) if cols % 4 == 0 else (0,)):
+                    plans = lr.lr_plan_enumerate(F, op, rows, cols, policy, aligned)
+                    plans.append(lr.lr_plan_for_device_ws(F, op, rows, cols, policy, aligned))
+                    for p in plans[:: max(1, len(plans) // 10)] + plans[-1:]:
+                        n = lr.lr_dispatch_rows(p, rows)
+                        assert 1 <= n <= rows
+                        if p.family == lr.LR_FAMILY_SPLIT:
+                            blocks = n * p.splits
+                        else:
+                            blocks = -(-n // p.rows_per_block)
+                            assert n == rows or n % p.rows_per_block == 0
+                        assert blocks * p.threads_per_block <= limit, (op, rows, cols, p)
+                        if rows * 64 * 16 <= limit:
+                            assert n == rows
+                        whole = rows * p.splits if p.family == lr.LR_FAMILY_SPLIT else -(-rows // p.rows_per_block)
+                        if whole * p.threads_per_block <= limit:
+                            assert n == rows  # never split without need
+                        else:
+                            assert (blocks + (p.splits or 1)) * p.threads_per_block > limit  # pieces are full
+                        checked += 1
+    assert checked > 500
+    # the grid of a tall, narrow problem does not fit one dispatch
+    p = lr.lr_plan_for_device(F, "softmax", (1 << 26) + 3, 1, "unordered_tree", 0)
+    assert lr.lr_dispatch_rows(p, (1 << 26) + 3) < (1 << 26) + 3
+    assert lr.lr_dispatch_rows(None, 5) == 0 and lr.lr_dispatch_rows(p, 0) == 0
