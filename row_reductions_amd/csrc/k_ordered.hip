@@ -57,7 +57,7 @@ __device__ __forceinline__ float contrib(float x, float ref) {
 // first is used, and a load past the row returns 0 (a store past it is
 // dropped).  An element loop that used each load at once would wait for one
 // memory round trip per element.
-constexpr int kPass = 8;
+constexpr int kPass = 16;
 
 __device__ __forceinline__ int pass_elem(int base, int u, int lane) { return base + kWave * u + lane; }
 
@@ -77,12 +77,31 @@ __device__ __forceinline__ float row_max(BufRes rx, int cols, int lane) {
 
 // Folds one full 256-entry slab into acc, left to right (FOLD_RIGHT: right to
 // left), one dependent add per entry.  The slab is read in 16-float groups
-// through a three-group rolling register buffer, group g+2's reads issued
-// with group g's adds, and scheduling-group barriers fix that interleave of
-// LDS reads and adds.  Left to the scheduler, the reads' placement varied
-// from kernel to kernel and the chain waited on LDS: the barriers made the
-// folds up to 17% faster on MI355X (768 x 6144: RMSNorm 33 -> 30 us,
-// LayerNorm 62-70 -> 58 us).
+// through a three-group rolling register buffer: group g+2's four reads are
+// issued before group g's sixteen adds, and scheduling barriers on both sides
+// of the adds keep them there.  Without the barriers the scheduler moved each
+// group's reads down next to their adds (reusing one register quad), and the
+// chain waited out the LDS latency once per group.  A wave issues one
+// instruction per slot, so the adds, reads and waits share the issue rate:
+// on MI355X a chain fed this way takes 6.7 cycles per add, against 8.3 with
+// the reads next to their adds and 4.3 for adds alone.
+// Ordering point of the fold: no LDS read crosses it (the empty asm
+// statement clobbers memory) and neither does the chain (the statement takes
+// and returns `acc`, so the adds before it come first and those after it
+// consume its result); the scheduling barrier keeps the machine scheduler
+// from moving anything else across.  It emits no instruction.
+__device__ __forceinline__ void fold_fence(float& acc) {
+    asm volatile("" : "+v"(acc)::"memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt operands that wait for the LDS counter alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14 and expcnt bits 6:4 at their maxima, lgkmcnt in
+// bits 11:8).
+constexpr int kWaitLgkm8 = 0xC07F | (8 << 8);
+constexpr int kWaitLgkm4 = 0xC07F | (4 << 8);
+constexpr int kWaitLgkm0 = 0xC07F;
+
 template <int POL>
 __device__ __forceinline__ float fold_full_slab(const float* slab, float acc) {
     const float4* s4 = reinterpret_cast<const float4*>(slab);
@@ -98,6 +117,15 @@ __device__ __forceinline__ float fold_full_slab(const float* slab, float acc) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         if (g + 2 < G) grp(g + 2, q[(g + 2) % 3]);
+        fold_fence(acc);
+        // one wait for the whole group: LDS reads complete in order, so
+        // leaving the later groups' reads (4 each) outstanding suffices
+        switch (min(2, G - 1 - g)) {
+            case 2: __builtin_amdgcn_s_waitcnt(kWaitLgkm8); break;
+            case 1: __builtin_amdgcn_s_waitcnt(kWaitLgkm4); break;
+            default: __builtin_amdgcn_s_waitcnt(kWaitLgkm0); break;
+        }
+        __builtin_amdgcn_sched_barrier(0);
         float4 (&cur)[4] = q[g % 3];
         if constexpr (POL == kPolFoldRight) {
 #pragma unroll
@@ -116,9 +144,7 @@ __device__ __forceinline__ float fold_full_slab(const float* slab, float acc) {
                 acc = acc + cur[i].w;
             }
         }
-        // per group: its four LDS reads (mask 0x100), then sixteen adds (VALU, 0x2)
-        if (g + 2 < G) __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x0002, 16, 0);
+        fold_fence(acc);
     }
     return acc;
 }
