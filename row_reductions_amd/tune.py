@@ -11,7 +11,11 @@ printed as a line for lr_plan_table.inc.
     python -m row_reductions_amd.tune --op layernorm --rows 768 --cols 6144
 
 Timing: `--sets` rotating input/output buffer sets (cold cache by default),
-`--iters` back-to-back launches on one stream between two HIP events.
+`--iters` back-to-back launches on one stream between two HIP events.  With
+`--graph` the `--iters` launches are captured in one HIP graph and replayed
+(three replays between the events): the per-launch time is then the GPU's
+and not the host's launch rate, which bounds eager calls near 4 us, so this
+is the mode for launch-bound shapes.
 """
 from __future__ import annotations
 
@@ -28,23 +32,24 @@ def _launcher(op, xs, ys, g, b, lab, rows, cols, eps, policy, sh, rs=None, ys2=N
     """run(i, plan): one launch on buffer set i; split plans use workspace ws."""
     pol = lr._policy(policy)
 
-    def run(i, plan):
+    def run(i, plan, stream=None):
+        sh_ = sh if stream is None else stream
         k = i % len(xs)
         w = ws if plan is not None and plan.family == lr.LR_FAMILY_SPLIT else None
         if op == "softmax":
-            return lr.lr_softmax_f32(xs[k], ys[k], rows, cols, pol, sh, plan, workspace=w)
+            return lr.lr_softmax_f32(xs[k], ys[k], rows, cols, pol, sh_, plan, workspace=w)
         if op == "rmsnorm":
-            return lr.lr_rmsnorm_f32(xs[k], g, ys[k], rows, cols, eps, pol, sh, plan, workspace=w)
+            return lr.lr_rmsnorm_f32(xs[k], g, ys[k], rows, cols, eps, pol, sh_, plan, workspace=w)
         if op == "layernorm":
-            return lr.lr_layernorm_f32(xs[k], g, b, ys[k], rows, cols, eps, pol, sh, plan, workspace=w)
+            return lr.lr_layernorm_f32(xs[k], g, b, ys[k], rows, cols, eps, pol, sh_, plan, workspace=w)
         if op == "add_layernorm":
-            return lr.lr_add_layernorm_f32(xs[k], rs[k], g, b, ys[k], None, rows, cols, eps, pol, sh, plan,
+            return lr.lr_add_layernorm_f32(xs[k], rs[k], g, b, ys[k], None, rows, cols, eps, pol, sh_, plan,
                                            workspace=w)
         if op == "row_sum":
-            return lr.lr_row_sum_f32(xs[k], ys[k], rows, cols, pol, sh, plan, workspace=w)
+            return lr.lr_row_sum_f32(xs[k], ys[k], rows, cols, pol, sh_, plan, workspace=w)
         if op == "row_minmax":
-            return lr.lr_row_minmax_f32(xs[k], ys[k], ys2[k], rows, cols, pol, sh, plan, workspace=w)
-        return lr.lr_cross_entropy_f32(xs[k], lab, ys[k], rows, cols, pol, sh, plan, workspace=w)
+            return lr.lr_row_minmax_f32(xs[k], ys[k], ys2[k], rows, cols, pol, sh_, plan, workspace=w)
+        return lr.lr_cross_entropy_f32(xs[k], lab, ys[k], rows, cols, pol, sh_, plan, workspace=w)
     return run
 
 
@@ -61,6 +66,29 @@ def _time(run, plan, iters, stream):
     return a.elapsed_time(z) * 1e3 / iters
 
 
+def _time_graph(run, plan, iters, stream, reps=3):
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        lr.check(run(0, plan, side.cuda_stream), "warmup")
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(iters):
+                run(i, plan, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    z.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return a.elapsed_time(z) * 1e3 / (iters * reps)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="exhaustive measured plan sweep for one shape")
     ap.add_argument("--op", required=True, choices=sorted(lr.OPS))
@@ -72,6 +100,7 @@ def main(argv=None):
     ap.add_argument("--iters", type=int, default=200)
     ap.add_argument("--max-rows-per-block", type=int, default=4)
     ap.add_argument("--json", action="store_true", help="one JSON line per candidate")
+    ap.add_argument("--graph", action="store_true", help="time HIP-graph replays (launch-bound shapes)")
     args = ap.parse_args(argv)
 
     dev = torch.device("cuda:0")
@@ -107,6 +136,7 @@ def main(argv=None):
     ref = ys[0].double().clone()
     bound = 1e-6 + 1e-5 * ref.abs()
 
+    timer = _time_graph if args.graph else _time
     results = []
     for p in lr.lr_plan_enumerate(facts, op, rows, cols, args.policy, aligned):
         if p.rows_per_block > args.max_rows_per_block:
@@ -114,18 +144,18 @@ def main(argv=None):
         st = run(0, p)
         torch.cuda.synchronize()
         valid = st == lr.LR_OK and bool(((ys[0].double() - ref).abs() <= bound).all())
-        us = _time(run, p, args.iters, stream) if valid else float("inf")
+        us = timer(run, p, args.iters, stream) if valid else float("inf")
         rec = dict(plan=p.as_dict(), us=us, valid=valid)
         results.append((us, p, rec))
         if args.json:
             print(json.dumps(rec), flush=True)
     results.sort(key=lambda t: t[0])
     best_us, best, _ = results[0]
-    again = _time(run, best, args.iters, stream)
+    again = timer(run, best, args.iters, stream)
     moved = {"cross_entropy": tensor_bytes + rows * 12, "add_layernorm": 3 * tensor_bytes,
              "row_sum": tensor_bytes + rows * 4, "row_minmax": tensor_bytes + rows * 8}.get(op, 2 * tensor_bytes)
-    print(f"# {op} {rows}x{cols} {args.policy}: {len(results)} candidates, "
-          f"automatic {_time(run, auto, args.iters, stream):.2f} us, "
+    print(f"# {op} {rows}x{cols} {args.policy}{' (graph)' if args.graph else ''}: {len(results)} candidates, "
+          f"automatic {timer(run, auto, args.iters, stream):.2f} us, "
           f"best {again:.2f} us ({moved / again / 1e3:.0f} GB/s): {best!r}")
     for us, p, rec in results[:8]:
         print(f"#   {us:8.2f} us  {p!r}")
