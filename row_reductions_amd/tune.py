@@ -89,6 +89,40 @@ def _time_graph(run, plan, iters, stream, reps=3):
     return a.elapsed_time(z) * 1e3 / (iters * reps)
 
 
+def _parse_plan(spec, enum, auto):
+    if spec == "auto":
+        return auto
+    f = spec.split(":")
+    fam = {name: code for code, name in lr.FAMILY_NAMES.items()}[f[0]]
+    want = (fam, *map(int, f[1:4]), int(f[4]) if len(f) > 4 else 0)
+    for p in enum:
+        if (p.family, p.waves_per_row, p.rows_per_block, p.chunks_per_lane, p.splits) == want:
+            return p
+    raise SystemExit(f"{spec}: not a legal plan of this problem")
+
+
+def _compare(args, op, rows, cols, aligned, facts, auto, run, ys, ref, bound, timer, stream):
+    """A/B of explicit plans: each round times every plan once, in alternating
+    order; medians (and minima) over the rounds."""
+    enum = lr.lr_plan_enumerate(facts, op, rows, cols, args.policy, aligned)
+    plans = [(spec, _parse_plan(spec, enum, auto)) for spec in args.compare]
+    for spec, p in plans:
+        st = run(0, p)
+        torch.cuda.synchronize()
+        if st != lr.LR_OK or not bool(((ys[0].double() - ref).abs() <= bound).all()):
+            raise SystemExit(f"{spec}: output differs from the automatic plan's")
+    times = {spec: [] for spec, _ in plans}
+    for r in range(args.rounds):
+        for spec, p in (plans if r % 2 == 0 else plans[::-1]):
+            times[spec].append(timer(run, p, args.iters, stream))
+    mode = "graph" if args.graph else "eager"
+    print(f"# {op} {rows}x{cols} {args.policy} ({mode}), A/B over {args.rounds} rounds: median us (min)")
+    for spec, p in plans:
+        v = sorted(times[spec])
+        print(f"#   {spec:22s} {v[len(v) // 2]:8.3f} ({v[0]:.3f})  {p!r}")
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="exhaustive measured plan sweep for one shape")
     ap.add_argument("--op", required=True, choices=sorted(lr.OPS))
@@ -101,6 +135,11 @@ def main(argv=None):
     ap.add_argument("--max-rows-per-block", type=int, default=4)
     ap.add_argument("--json", action="store_true", help="one JSON line per candidate")
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays (launch-bound shapes)")
+    ap.add_argument("--compare", nargs="+", metavar="PLAN",
+                    help="instead of the sweep: A/B of the given plans, alternating for --rounds rounds; "
+                         "PLAN is 'auto' (the typed entry points' plan) or family:S:Q:chunks[:splits], "
+                         "family one of cache, stream, ordered, tree, split")
+    ap.add_argument("--rounds", type=int, default=6)
     args = ap.parse_args(argv)
 
     dev = torch.device("cuda:0")
@@ -137,6 +176,8 @@ def main(argv=None):
     bound = 1e-6 + 1e-5 * ref.abs()
 
     timer = _time_graph if args.graph else _time
+    if args.compare:
+        return _compare(args, op, rows, cols, aligned, facts, auto, run, ys, ref, bound, timer, stream)
     results = []
     for p in lr.lr_plan_enumerate(facts, op, rows, cols, args.policy, aligned):
         if p.rows_per_block > args.max_rows_per_block:
