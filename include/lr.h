@@ -103,7 +103,10 @@ typedef enum lr_op {
 /* Kernel families.
  * CACHE:   each lane keeps its stripe of the row in registers (VGPRs), so
  *          the row is read from memory once and every later pass reads
- *          registers (the pages' worker-private stripe, section 5).
+ *          registers (the pages' worker-private stripe, section 5).  Narrow
+ *          rows may take sub-wave teams: lanes_per_row = 4, 8, 16 or 32
+ *          lanes serve one row, so one wavefront holds 64 / lanes_per_row
+ *          rows and its cross-lane reductions stop at the team's width.
  * STREAM:  no register copy; passes that need the row again reload it
  *          (softmax and cross-entropy fold max and sum-of-exp in one
  *          online pass).  Any row length.
@@ -132,11 +135,15 @@ typedef enum lr_family {
 } lr_family;
 
 /* A launch plan (the pages' GroupPlan decision record, section 2, mapped to
- * wave64: workers per row W = 64 * waves_per_row, section 4). */
+ * wave64: workers per row W = lanes_per_row = 64 * waves_per_row, or a
+ * sub-wave team of a CACHE plan, section 4). */
 typedef struct lr_plan {
     int32_t family;            /* lr_family */
-    int32_t waves_per_row;     /* S: wavefronts cooperating on one row, 1..16 */
-    int32_t rows_per_block;    /* Q: rows packed into one workgroup, S*Q <= 16 */
+    int32_t waves_per_row;     /* S: wavefronts cooperating on one row, 1..16
+                                  (1 for a sub-wave team) */
+    int32_t rows_per_block;    /* Q: rows packed into one workgroup, S*Q <= 16;
+                                  sub-wave teams: a multiple of
+                                  64 / lanes_per_row, lanes_per_row * Q <= 1024 */
     int32_t vec;               /* V: consecutive FP32 a lane owns per chunk (4 = 128-bit) */
     int32_t chunks_per_lane;   /* CACHE: 128-bit chunks held per lane (a compiled
                                   instance: 1,2,3,4,6,8,12,16,24 or 32);
@@ -144,13 +151,19 @@ typedef struct lr_plan {
                                   (1,2,3,4,6 or 8);
                                   STREAM: chunks loaded per lane per loop trip;
                                   ORDERED: 0 */
-    int32_t threads_per_block; /* 64 * S * Q */
+    int32_t threads_per_block; /* 64 * S * Q, or lanes_per_row * Q */
     int64_t blocks;            /* ceil(rows / Q); SPLIT: rows * splits */
     int32_t lds_bytes;         /* static LDS the kernel uses */
     int32_t reductions;        /* |R|: cross-lane reductions per row */
     int32_t row_aligned;       /* 1: planned for 16-byte aligned rows */
     int32_t splits;            /* SPLIT: segments per row, 2..64 (Q = 1);
                                   0 for every other family */
+    int32_t lanes_per_row;     /* lanes serving one row: 64 * S (0 reads as
+                                  64 * S, so a plan filled in field by field
+                                  without it keeps whole waves), or 4, 8, 16
+                                  or 32 for a CACHE plan of sub-wave teams
+                                  (S = 1, chunks_per_lane 1 or 2); the
+                                  planner always fills it in */
 } lr_plan;
 
 /* What the planner needs to know about a device. */
@@ -196,7 +209,9 @@ lr_status lr_layernorm_f32(const float* x, const float* gamma, const float* beta
  * cross-entropy source; section 5.2 guarded gather):
  *   m = max_k x[r][k];  s = sum_k exp(x[r][k] - m);
  *   sel = (0 <= labels[r] < cols) ? x[r][labels[r]] : 0   (int64 compare);
- *   losses[r] = log(s) + m - sel.
+ *   losses[r] = log(s) + (m - sel), the difference first (exact in FP32
+ *   whenever sel >= m / 2, so a small loss next to large logits keeps its
+ *   accuracy).
  * logits: rows*cols FP32; labels: rows int64 (any value: out-of-range labels
  * are not an error, they select 0); losses: rows FP32 out. */
 lr_status lr_cross_entropy_f32(const float* logits, const int64_t* labels,

@@ -62,6 +62,7 @@ class LrPlan(ctypes.Structure):
         ("reductions", ctypes.c_int32),
         ("row_aligned", ctypes.c_int32),
         ("splits", ctypes.c_int32),
+        ("lanes_per_row", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

@@ -259,7 +259,7 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
             if (lane == 0) {
                 const int64_t lab = a.labels[row];
                 const float sel = (lab >= 0 && lab < (int64_t)cols) ? xr[lab] : 0.0f;
-                a.losses[row] = (logf(s) + m) - sel;
+                a.losses[row] = logf(s) + (m - sel);
             }
         } else {
             const BufRes ry = make_res(a.y + row * (int64_t)cols, cols * 4);

@@ -76,6 +76,29 @@ __device__ __forceinline__ float wave_allreduce(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
+// All-reduce over aligned groups of L lanes (L = 4, 8, 16, 32 or 64): the
+// first log2(L) steps of the wave64 all-reduce above, after which every lane
+// of a group holds the group's total (with the same bits in every lane of
+// the group).  The result may differ between groups, so it stays per lane.
+template <class R, int L>
+__device__ __forceinline__ float group_allreduce(float v) {
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "group of 4 .. 64 lanes");
+    if constexpr (L == kWave) {
+        return wave_allreduce<R>(v);
+    } else {
+        v = R::apply(v, dpp_mov<0xB1>(v));                        // quad_perm [1,0,3,2]
+        v = R::apply(v, dpp_mov<0x4E>(v));                        // quad_perm [2,3,0,1]
+        if constexpr (L >= 8) v = R::apply(v, dpp_mov<0x141>(v));  // row_half_mirror
+        if constexpr (L >= 16) v = R::apply(v, dpp_mov<0x140>(v)); // row_mirror
+        if constexpr (L >= 32) {
+            const unsigned b = __builtin_bit_cast(unsigned, v);
+            auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+            v = R::apply(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+        }
+        return v;
+    }
+}
+
 // Reduction over a row team of S wavefronts ("TIRx Metal reduction
 // lowering", section 4.2 protocol): wave collective in every wave, lane 0
 // publishes its wave's partial to LDS, one workgroup barrier, then every wave

@@ -40,6 +40,9 @@ struct KArgs {
 constexpr int kCacheChunks[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
 constexpr int kNumCacheChunks = sizeof(kCacheChunks) / sizeof(kCacheChunks[0]);
 constexpr int kStreamUnroll = 4;
+// Chunk counts of the sub-wave CACHE instances (lanes_per_row 4 .. 32), ascending.
+constexpr int kNarrowChunks[] = {1, 2};
+constexpr int kNumNarrowChunks = sizeof(kNarrowChunks) / sizeof(kNarrowChunks[0]);
 // Split-family chunk counts (the stripe of one segment), ascending.
 constexpr int kSplitChunks[] = {1, 2, 3, 4, 6, 8};
 constexpr int kNumSplitChunks = sizeof(kSplitChunks) / sizeof(kSplitChunks[0]);

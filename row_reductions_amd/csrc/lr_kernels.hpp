@@ -3,7 +3,10 @@
 // the k_<op>.hip translation units.
 //
 // Roles of the steps ("TIRx Metal reduction lowering"):
-//   section 1   softmax: exp(x - max) / sum;  cross-entropy: log(sum) + max - selected
+//   section 1   softmax: exp(x - max) / sum;  cross-entropy: log(sum) + (max - selected),
+//               the difference first: it is exact whenever selected >= max / 2
+//               (Sterbenz), so a confident prediction's small loss is not lost
+//               in the rounding of max + log(sum)
 //   section 4   S waves cooperate on a row, Q rows share a workgroup
 //   section 4.4 blocked-cyclic ownership, V = 4 (one 128-bit access per chunk)
 //   section 5   the row's chunks are kept per worker (here: in VGPRs) so every
@@ -31,12 +34,24 @@ __device__ __forceinline__ float fmaxnum(float a, float b) { return __builtin_fm
 
 // Writes the row's minimum and maximum after the stripe folds: a lane that
 // held no element of the row still has NaN and takes the identities.
+// A row's team reduction: S cooperating waves (LW = 64), or a sub-wave team
+// of LW lanes (one DPP group, no LDS).
+template <class R, int LW>
+__device__ __forceinline__ float row_reduce(float v, float* slots, int S, const Team& t) {
+    if constexpr (LW < kWave) {
+        return group_allreduce<R, LW>(v);
+    } else {
+        return team_reduce<R>(v, slots, S, t);
+    }
+}
+
+template <int LW = kWave>
 __device__ __forceinline__ void finish_minmax(const KArgs& a, float lo, float hi, float* red_lo, float* red_hi,
                                               int S, const Team& t, bool active, int64_t row) {
     lo = __builtin_isnan(lo) ? INFINITY : lo;
     hi = __builtin_isnan(hi) ? -INFINITY : hi;
-    lo = team_reduce<MinOp>(lo, red_lo, S, t);
-    hi = team_reduce<MaxOp>(hi, red_hi, S, t);
+    lo = row_reduce<MinOp, LW>(lo, red_lo, S, t);
+    hi = row_reduce<MaxOp, LW>(hi, red_hi, S, t);
     if (active && t.w == 0) {
         if (a.mins) a.mins[row] = lo;
         if (a.maxs) a.maxs[row] = hi;
@@ -70,12 +85,13 @@ __device__ __forceinline__ void store_chunk(float* dr, bool same_phase, int k, i
 // Chunk k of a row that sits at its own (unknown) phase, read one float at a
 // time at clamped, in-range indexes of the x row's grid (phase h); grid slots
 // outside [0, cols) hold some element of the row and must not be used.
-__device__ __forceinline__ float4 elem_chunk(BufRes r, int k, int h, int cols) {
+// `base`: byte offset of the row within the resource.
+__device__ __forceinline__ float4 elem_chunk(BufRes r, int k, int h, int cols, int base = 0) {
     float4 g;
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
         const int e = min(max(elem_index(k, j, h), 0), cols - 1);
-        set(g, j, res_ld1(r, e * 4));
+        set(g, j, res_ld1(r, base + e * 4));
     }
     return g;
 }
@@ -150,41 +166,64 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // reduction, was 0.3-2 us slower; rotating each workgroup's chunk order to
 // spread those requests cost more in the row stream than it saved.
 // ===========================================================================
-template <int OP, int NCH, bool AL, int PM>
-__global__ void __launch_bounds__(cache_max_threads(NCH))
-k_cache(const KArgs a) {
-    __shared__ float red[2][kMaxWaves];
+// The body of both CACHE kernels.  LW = 64: a row team of S waves (k_cache).
+// LW = 4, 8, 16 or 32: sub-wave teams for narrow rows (k_cache_narrow), 64 /
+// LW rows per wave.  Row, phase and chunk count are then per lane, and the
+// row is read through one resource per wave covering all its rows: a lane's
+// chunk k sits at byte xo + 16 k, xo being its row's 16-byte grid base
+// relative to the wave's first row's.  Past a row's chunks that resource
+// holds the next row, so every slot past the row takes the identity.
+template <int OP, int NCH, bool AL, int PM, int LW>
+__device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxWaves]) {
+    constexpr bool NARROW = LW < kWave;
     constexpr float ID = op_identity<OP>();
     constexpr int NP = num_params<OP>();
-    const int S = a.S;
-    const int W = kWave * S;
-    const Team t = team_of_wave(wave_id(), (int)threadIdx.x & (kWave - 1), S, a.team_magic);
+    const int S = NARROW ? 1 : a.S;
+    const int W = NARROW ? LW : kWave * S;
+    const int lane = (int)threadIdx.x & (kWave - 1);
+    const Team t = NARROW ? team_of_group(wave_id(), lane, LW) : team_of_wave(wave_id(), lane, S, a.team_magic);
     const int64_t row = row_of(blockIdx.x, a.Q, t.q);
     const bool active = row < a.rows;
     const int cols = a.cols;
     const float* xr = a.x + (active ? row : 0) * (int64_t)cols;
     const int h = AL ? 0 : phase_of(reinterpret_cast<uintptr_t>(xr));
     const int nv = active ? (AL ? cols / kVec : chunks_of(h, cols)) : 0;
-    const BufRes rx = make_res(xr - h, nv * 16);
     const BufRes rg = make_res(a.gamma, NP >= 1 && a.gamma ? cols * 4 : 0);
     const BufRes rb = make_res(a.beta, NP == 2 && a.beta ? cols * 4 : 0);
     // fused residual: aligned rows read it on the x grid, misaligned rows one
     // float at a time (its phase need not match x's)
     constexpr bool RES = OP == kAddLayerNorm;
     const int64_t roff = (active ? row : 0) * (int64_t)cols;
-    const BufRes rr = make_res(RES ? a.residual + roff : nullptr, RES && active ? (AL ? nv * 16 : cols * 4) : 0);
+    BufRes rx, rr;
+    int xo = 0, ro = 0;  // byte offsets of this lane's row in rx and rr
+    if constexpr (!NARROW) {
+        rx = make_res(xr - h, nv * 16);
+        rr = make_res(RES ? a.residual + roff : nullptr, RES && active ? (AL ? nv * 16 : cols * 4) : 0);
+    } else {
+        const int64_t r0 = row_of(blockIdx.x, a.Q, wave_id() * (kWave / LW));  // the wave's first row
+        const int64_t left = a.rows - r0;
+        const int nr = left <= 0 ? 0 : (left < kWave / LW ? (int)left : kWave / LW);  // its rows that exist
+        const int64_t off0 = (nr > 0 ? r0 : 0) * (int64_t)cols;
+        const int h0 = AL ? 0 : phase_of(reinterpret_cast<uintptr_t>(a.x + off0));
+        const int xbytes = (nr * cols + h0 + kVec - 1) / kVec * 16;
+        rx = make_res(a.x + off0 - h0, xbytes);
+        xo = active ? (int)(((row - r0) * cols - h + h0) * 4) : 0;
+        rr = make_res(RES ? a.residual + off0 : nullptr, RES ? (AL ? xbytes : nr * cols * 4) : 0);
+        ro = active ? (int)((row - r0) * cols * 4) : 0;
+    }
     auto chunk = [&](int c) { return chunk_index(t.w, W, c); };
 
     float4 v[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int k = chunk(c);
-        float4 raw = res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rx, k * 16);
+        float4 raw = res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rx, xo + k * 16);
         if constexpr (RES) {
-            const float4 q = AL ? res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rr, k * 16) : elem_chunk(rr, k, h, cols);
+            const float4 q = AL ? res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rr, ro + k * 16)
+                                : elem_chunk(rr, k, h, cols, ro);
             raw = make_float4(raw.x + q.x, raw.y + q.y, raw.z + q.z, raw.w + q.w);
         }
-        if constexpr (ID == 0.0f && AL) {
+        if constexpr (ID == 0.0f && AL && !NARROW) {
             v[c] = raw;  // past the end: zeros, the add identity
         } else {
             v[c] = (k < nv) ? raw : splat4(ID);
@@ -205,7 +244,7 @@ k_cache(const KArgs a) {
         float m = ID;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) m = fmax2(fmax2(m, fmax2(v[c].x, v[c].y)), fmax2(v[c].z, v[c].w));
-        m = wave_allreduce<MaxOp>(m);
+        m = group_allreduce<MaxOp, LW>(m);
         float s = 0.0f;
         if (m != -INFINITY) {  // a wave with no element of the row keeps (-inf, 0)
 #pragma unroll
@@ -217,10 +256,10 @@ k_cache(const KArgs a) {
                 s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
             }
         }
-        s = wave_allreduce<AddOp>(s);
+        s = group_allreduce<AddOp, LW>(s);
         const MaxSum ms = team_maxsum(m, s, red[0], red[1], S, t);
         if constexpr (OP == kCrossEntropy) {
-            if (active && t.w == 0) a.losses[row] = (fast_log(ms.s) + ms.m) - sel;
+            if (active && t.w == 0) a.losses[row] = fast_log(ms.s) + (ms.m - sel);
         } else {
             // y = exp(x - m_w) * exp(m_w - M) / s
             const float r = (m == -INFINITY) ? 0.0f : fast_exp(m - ms.m) * fast_rcp(ms.s);
@@ -238,7 +277,7 @@ k_cache(const KArgs a) {
         float sum = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) sum += (v[c].x + v[c].y) + (v[c].z + v[c].w);
-        sum = team_reduce<AddOp>(sum, red[0], S, t);
+        sum = row_reduce<AddOp, LW>(sum, red[0], S, t);
         if (active && t.w == 0) a.sums[row] = sum;
     } else if constexpr (OP == kRowMinMax) {
         float lo = ID, hi = ID;
@@ -247,13 +286,13 @@ k_cache(const KArgs a) {
             lo = fminnum(fminnum(lo, fminnum(v[c].x, v[c].y)), fminnum(v[c].z, v[c].w));
             hi = fmaxnum(fmaxnum(hi, fmaxnum(v[c].x, v[c].y)), fmaxnum(v[c].z, v[c].w));
         }
-        finish_minmax(a, lo, hi, red[0], red[1], S, t, active, row);
+        finish_minmax<LW>(a, lo, hi, red[0], red[1], S, t, active, row);
     } else if constexpr (OP == kRmsNorm) {
         float ss = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
             ss += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
-        ss = team_reduce<AddOp>(ss, red[0], S, t);
+        ss = row_reduce<AddOp, LW>(ss, red[0], S, t);
         const float r = fast_rsqrt(ss * a.inv_cols + a.eps);
         float* yr = a.y + row * (int64_t)cols;
 #pragma unroll
@@ -280,7 +319,7 @@ k_cache(const KArgs a) {
                 }
             }
         }
-        sum = team_reduce<AddOp>(sum, red[0], S, t);
+        sum = row_reduce<AddOp, LW>(sum, red[0], S, t);
         const float mu = sum * a.inv_cols;
         float qs = 0.0f;
 #pragma unroll
@@ -292,7 +331,7 @@ k_cache(const KArgs a) {
             v[c] = d;
             qs += (d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w);
         }
-        qs = team_reduce<AddOp>(qs, red[1], S, t);
+        qs = row_reduce<AddOp, LW>(qs, red[1], S, t);
         const float r = fast_rsqrt(qs * a.inv_cols + a.eps);
         float* yr = a.y + row * (int64_t)cols;
 #pragma unroll
@@ -307,6 +346,21 @@ k_cache(const KArgs a) {
             }
         }
     }
+}
+
+template <int OP, int NCH, bool AL, int PM>
+__global__ void __launch_bounds__(cache_max_threads(NCH))
+k_cache(const KArgs a) {
+    __shared__ float red[2][kMaxWaves];
+    cache_body<OP, NCH, AL, PM, kWave>(a, red);
+}
+
+// Sub-wave teams: LW lanes per row, 64 / LW rows per wave, S = 1.
+template <int OP, int NCH, bool AL, int PM, int LW>
+__global__ void __launch_bounds__(1024)
+k_cache_narrow(const KArgs a) {
+    __shared__ float red[2][kMaxWaves];  // untouched: no cross-wave exchange
+    cache_body<OP, NCH, AL, PM, LW>(a, red);
 }
 
 // ===========================================================================
@@ -375,7 +429,7 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
         const float sc = (m == -INFINITY) ? 0.0f : s * fast_exp(m - M);
         const float tot = team_reduce<AddOp>(sc, red[1], S, t);
         if constexpr (OP == kCrossEntropy) {
-            if (active && t.w == 0) a.losses[row] = (fast_log(tot) + M) - sel;
+            if (active && t.w == 0) a.losses[row] = fast_log(tot) + (M - sel);
         } else {
             const float r = fast_rcp(tot);
             for (int k0 = t.w; k0 < nv; k0 += W * U) {
@@ -495,8 +549,31 @@ hipError_t launch_cache_inst(const KArgs& a, const lr_plan& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int OP, int NCH, bool AL, int PM, int LW>
+hipError_t launch_narrow_inst(const KArgs& a, const lr_plan& p, hipStream_t s) {
+    hipLaunchKernelGGL((k_cache_narrow<OP, NCH, AL, PM, LW>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+template <int OP, bool AL, int PM, int LW>
+hipError_t launch_narrow_nch(const KArgs& a, const lr_plan& p, hipStream_t s) {
+    switch (p.chunks_per_lane) {
+        case 1: return launch_narrow_inst<OP, 1, AL, PM, LW>(a, p, s);
+        case 2: return launch_narrow_inst<OP, 2, AL, PM, LW>(a, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int OP, bool AL, int PM>
 hipError_t launch_cache_nch(const KArgs& a, const lr_plan& p, hipStream_t s) {
+    switch (p.lanes_per_row) {
+        case 4: return launch_narrow_nch<OP, AL, PM, 4>(a, p, s);
+        case 8: return launch_narrow_nch<OP, AL, PM, 8>(a, p, s);
+        case 16: return launch_narrow_nch<OP, AL, PM, 16>(a, p, s);
+        case 32: return launch_narrow_nch<OP, AL, PM, 32>(a, p, s);
+        default: break;  // whole-wave teams
+    }
     switch (p.chunks_per_lane) {
         case 1: return launch_cache_inst<OP, 1, AL, PM>(a, p, s);
         case 2: return launch_cache_inst<OP, 2, AL, PM>(a, p, s);

@@ -55,6 +55,15 @@ LR_HD Team team_of_wave(int wave, int lane, int S, int magic) {
 
 LR_HD Team team_of(int tid, int S) { return team_of_wave(tid / kWave, tid % kWave, S, team_magic(S)); }
 
+// Sub-wave teams of L = 4, 8, 16 or 32 lanes (CACHE family, narrow rows):
+// lane group lane / L of wave `wave` serves packed row wave * (64 / L) +
+// lane / L, as worker lane % L.
+constexpr int kNarrowLanes[] = {4, 8, 16, 32};
+
+LR_HD bool narrow_lanes(int L) { return L == 4 || L == 8 || L == 16 || L == 32; }
+
+LR_HD Team team_of_group(int wave, int lane, int L) { return Team{wave * (kWave / L) + lane / L, lane % L, 0, lane}; }
+
 LR_HD int64_t row_of(int64_t block, int Q, int q) { return block * Q + q; }
 
 // Floats between the 16-byte boundary at or below `addr` and `addr`.

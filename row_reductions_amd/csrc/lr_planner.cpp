@@ -78,8 +78,21 @@ static int smallest_cache_instance(int64_t need) {
     return 0;
 }
 
+static bool narrow_chunks_compiled(int nch) {
+    for (int i = 0; i < kNumNarrowChunks; ++i)
+        if (kNarrowChunks[i] == nch) return true;
+    return false;
+}
+
+static int smallest_narrow_instance(int64_t need) {
+    for (int i = 0; i < kNumNarrowChunks; ++i)
+        if (kNarrowChunks[i] >= need) return kNarrowChunks[i];
+    return 0;
+}
+
+// `lanes`: 4, 8, 16 or 32 for a CACHE plan of sub-wave teams (S = 1), else 0.
 static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_t cols, int op, bool aligned,
-                        int splits = 0) {
+                        int splits = 0, int lanes = 0) {
     lr_plan p;
     std::memset(&p, 0, sizeof(p));
     p.family = family;
@@ -87,7 +100,8 @@ static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_
     p.rows_per_block = Q;
     p.vec = family == LR_FAMILY_ORDERED ? 1 : kVec;
     p.chunks_per_lane = nch;
-    p.threads_per_block = kWave * S * Q;
+    p.lanes_per_row = lanes != 0 ? lanes : kWave * S;
+    p.threads_per_block = lanes != 0 ? lanes * Q : kWave * S * Q;
     p.splits = family == LR_FAMILY_SPLIT ? splits : 0;
     p.blocks = family == LR_FAMILY_SPLIT ? rows * splits : (rows + Q - 1) / Q;
     p.reductions = reductions_of(op);
@@ -127,11 +141,22 @@ lr_status validate_plan(const lr_device_facts* f, int op, int64_t rows, int64_t 
     lr_status st = check_problem(f, op, rows, cols, policy);
     if (st != LR_OK) return st;
     if (p == nullptr) return LR_ERR_NULL_POINTER;
-    const int S = p->waves_per_row, Q = p->rows_per_block;
+    const int S = p->waves_per_row, Q = p->rows_per_block, L = p->lanes_per_row;
+    if (!family_allowed(policy, p->family)) return LR_ERR_UNREALIZABLE_PLAN;
+    if (narrow_lanes(L)) {
+        // sub-wave teams: CACHE only, one team per L lanes, whole waves per
+        // workgroup, a compiled stripe that covers the widest row
+        if (p->family != LR_FAMILY_CACHE || S != 1 || Q < 1 || Q % (kWave / L) != 0) return LR_ERR_UNREALIZABLE_PLAN;
+        if ((int64_t)L * Q > f->max_threads_per_block || p->threads_per_block != L * Q) return LR_ERR_UNREALIZABLE_PLAN;
+        if (p->splits != 0 || p->blocks != (rows + Q - 1) / Q || p->blocks > INT32_MAX) return LR_ERR_UNREALIZABLE_PLAN;
+        if (p->vec != kVec || !narrow_chunks_compiled(p->chunks_per_lane)) return LR_ERR_UNREALIZABLE_PLAN;
+        if (p->chunks_per_lane < (max_row_chunks(cols, aligned) + L - 1) / L) return LR_ERR_UNREALIZABLE_PLAN;
+        return LR_OK;
+    }
     if (S < 1 || Q < 1 || S > kMaxWaves || Q > kMaxWaves || S * Q > kMaxWaves) return LR_ERR_UNREALIZABLE_PLAN;
+    if (L != 0 && L != kWave * S) return LR_ERR_UNREALIZABLE_PLAN;  // 0: whole waves
     if (p->threads_per_block != kWave * S * Q || p->threads_per_block > f->max_threads_per_block)
         return LR_ERR_UNREALIZABLE_PLAN;
-    if (!family_allowed(policy, p->family)) return LR_ERR_UNREALIZABLE_PLAN;
     if (p->family == LR_FAMILY_SPLIT) {
         // one segment per workgroup; every lane of a merging wave holds one
         // partial, and no row has fewer chunks than segments
@@ -195,6 +220,13 @@ static int enumerate_all(const lr_device_facts* f, int op, int64_t rows, int64_t
         if (nch == 0) continue;
         for (int Q = 1; S * Q <= kMaxWaves; ++Q) push(make_plan(LR_FAMILY_CACHE, S, Q, nch, rows, cols, op, aligned));
     }
+    // sub-wave teams for narrow rows: L lanes per row, 1 .. 16 waves per workgroup
+    for (int L : kNarrowLanes) {
+        const int nch = smallest_narrow_instance((nv + L - 1) / L);
+        if (nch == 0) continue;
+        for (int w = 1; w <= kMaxWaves; ++w)
+            push(make_plan(LR_FAMILY_CACHE, 1, w * (kWave / L), nch, rows, cols, op, aligned, 0, L));
+    }
     for (int S = 1; S <= kMaxWaves; ++S)
         for (int Q = 1; S * Q <= kMaxWaves; ++Q)
             push(make_plan(LR_FAMILY_STREAM, S, Q, kStreamUnroll, rows, cols, op, aligned));
@@ -229,6 +261,7 @@ struct TableEntry {
     int aligned;
     int family, S, Q, nch;
     int splits;  // SPLIT entries only
+    int lanes;   // sub-wave CACHE entries only (0: whole waves)
 };
 
 static const TableEntry kTable[] = {
@@ -267,7 +300,7 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
         return e.op == op && e.policy == policy && e.rows == rows && e.cols == cols && e.aligned == (aligned ? 1 : 0);
     };
     auto from_entry = [&](const TableEntry& e) {
-        return make_plan(e.family, e.S, e.Q, e.nch, rows, cols, op, aligned, e.splits);
+        return make_plan(e.family, e.S, e.Q, e.nch, rows, cols, op, aligned, e.splits, e.lanes);
     };
     if (allow_split && policy == LR_UNORDERED_TREE) {
         // a measured SPLIT winner; else the split prior, unless a measured
@@ -308,6 +341,15 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
         }
         const int Q = rows >= 4 * simds ? 4 : 1;
         return make_plan(LR_FAMILY_ORDERED, 1, Q, 0, rows, cols, op, aligned);
+    }
+    if (S == 1 && nv <= 32) {
+        // rows plentiful and narrow: sub-wave teams with one chunk per lane
+        // (the smallest power of two lanes from 4 to 32 that covers the row),
+        // four waves per workgroup
+        int L = 4;
+        while (L < nv) L *= 2;
+        lr_plan p = make_plan(LR_FAMILY_CACHE, 1, 4 * (kWave / L), 1, rows, cols, op, aligned, 0, L);
+        if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
     }
     int family = LR_FAMILY_CACHE;
     int nch = smallest_cache_instance(need(S));
@@ -391,8 +433,10 @@ extern "C" lr_status lr_coverage_check(const lr_plan* p, int64_t rows, int64_t c
     if (p == nullptr || counts == nullptr) return LR_ERR_NULL_POINTER;
     if (rows < 0 || cols < 1 || cols >= (int64_t(1) << 24)) return LR_ERR_INVALID_SHAPE;
     if (phase < 0 || phase > 3) return LR_ERR_INVALID_ARGUMENT;
-    const int S = p->waves_per_row, Q = p->rows_per_block;
-    if (S < 1 || Q < 1 || p->threads_per_block != kWave * S * Q) return LR_ERR_UNREALIZABLE_PLAN;
+    const int S = p->waves_per_row, Q = p->rows_per_block, L = p->lanes_per_row;
+    const bool narrow = narrow_lanes(L);
+    if (S < 1 || Q < 1 || p->threads_per_block != (narrow ? L * Q : kWave * S * Q)) return LR_ERR_UNREALIZABLE_PLAN;
+    if (narrow && (p->family != LR_FAMILY_CACHE || S != 1)) return LR_ERR_UNREALIZABLE_PLAN;
     const int c = (int)cols;
     if (p->family == LR_FAMILY_SPLIT && (p->splits < 1 || Q != 1)) return LR_ERR_UNREALIZABLE_PLAN;
     for (int64_t b = 0; b < p->blocks; ++b) {
@@ -427,8 +471,8 @@ extern "C" lr_status lr_coverage_check(const lr_plan* p, int64_t rows, int64_t c
                     }
                 continue;
             }
-            const Team t = team_of(tid, S);
-            const int W = kWave * S;
+            const Team t = narrow ? team_of_group(tid / kWave, tid % kWave, L) : team_of(tid, S);
+            const int W = narrow ? L : kWave * S;
             const int64_t row = row_of(b, Q, t.q);
             if (row >= rows) continue;
             const int h = (int)((phase + (row * cols) % kVec) % kVec);

@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(kMergeWaves * kWave) k_split_merge(const KArgs
     const RowStats st = merge_partials<OP>(a, q, lane, 0, 0);
     if (lane == 0) {
         if constexpr (OP == kCrossEntropy) {
-            a.losses[row] = (fast_log(st.b) + st.a) - gather_label(a, xr, row);
+            a.losses[row] = fast_log(st.b) + (st.a - gather_label(a, xr, row));
         } else if constexpr (OP == kRowSum) {
             a.sums[row] = st.a;
         } else {

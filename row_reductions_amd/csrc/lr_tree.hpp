@@ -108,7 +108,7 @@ k_tree(const KArgs a) {
         if constexpr (OP == kCrossEntropy) {
             if (active && t.w == 0) {
                 const float sel = gather_label(a, xr, row);
-                a.losses[row] = (logf(s) + m) - sel;
+                a.losses[row] = logf(s) + (m - sel);
             }
         } else {
 #pragma unroll

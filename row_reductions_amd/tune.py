@@ -94,9 +94,13 @@ def _parse_plan(spec, enum, auto):
         return auto
     f = spec.split(":")
     fam = {name: code for code, name in lr.FAMILY_NAMES.items()}[f[0]]
-    want = (fam, *map(int, f[1:4]), int(f[4]) if len(f) > 4 else 0)
+    S, Q, nch = map(int, f[1:4])
+    n = int(f[4]) if len(f) > 4 else 0
+    splits = n if fam == lr.LR_FAMILY_SPLIT else 0
+    lanes = n if fam == lr.LR_FAMILY_CACHE and n else 64 * S
     for p in enum:
-        if (p.family, p.waves_per_row, p.rows_per_block, p.chunks_per_lane, p.splits) == want:
+        if (p.family, p.waves_per_row, p.rows_per_block, p.chunks_per_lane, p.splits, p.lanes_per_row) == \
+                (fam, S, Q, nch, splits, lanes):
             return p
     raise SystemExit(f"{spec}: not a legal plan of this problem")
 
@@ -137,8 +141,9 @@ def main(argv=None):
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays (launch-bound shapes)")
     ap.add_argument("--compare", nargs="+", metavar="PLAN",
                     help="instead of the sweep: A/B of the given plans, alternating for --rounds rounds; "
-                         "PLAN is 'auto' (the typed entry points' plan) or family:S:Q:chunks[:splits], "
-                         "family one of cache, stream, ordered, tree, split")
+                         "PLAN is 'auto' (the typed entry points' plan) or family:S:Q:chunks[:N], "
+                         "family one of cache, stream, ordered, tree, split; N is the split count of a "
+                         "split plan, the lanes per row of a sub-wave cache plan")
     ap.add_argument("--rounds", type=int, default=6)
     args = ap.parse_args(argv)
 
@@ -209,6 +214,8 @@ def main(argv=None):
 
     def table_line(p):
         tail = f", {p.splits}" if p.family == lr.LR_FAMILY_SPLIT else ""
+        if p.lanes_per_row < 64:
+            tail = f", 0, {p.lanes_per_row}"
         return (f"{{{opn}, {pol}, {rows}, {cols}, {aligned}, {fam[p.family]}, {p.waves_per_row}, "
                 f"{p.rows_per_block}, {p.chunks_per_lane}{tail}}},")
     # the best plan, and the best that needs no workspace (the typed entry

@@ -138,3 +138,29 @@ def check_output(op: str, inp: dict, eps, policy: str, got: np.ndarray, what: st
         raise AssertionError(f"{what}: differs from the FP32 replay at {tuple(bad)}: "
                              f"gpu={got[tuple(bad)]!r} replay={rep[tuple(bad)]!r}")
     return 0.0
+
+
+GUARD = 16                  # floats of guard on each side of a placed tensor
+CANARY = -1.5 * 2.0 ** 126  # guard value (exact in FP32)
+
+
+def placed(a, off):
+    """`a` (float32) on the device `off` floats past a 16-byte boundary,
+    between guard regions of CANARY: (view, whole buffer)."""
+    flat = np.ascontiguousarray(a, dtype=np.float32).reshape(-1)
+    full = torch.full((flat.size + 2 * GUARD + off,), CANARY, dtype=torch.float32, device=DEV)
+    view = full[GUARD + off:GUARD + off + flat.size]
+    view.copy_(torch.from_numpy(flat).to(DEV))
+    return view.view(a.shape), full
+
+
+def guards_intact(view, full):
+    f = full.cpu().numpy()
+    start = view.storage_offset() - full.storage_offset()
+    return bool((f[:start] == CANARY).all() and (f[start + view.numel():] == CANARY).all())
+
+
+def bits_equal(got, rep, what):
+    if not np.array_equal(got.view(np.uint32), rep.view(np.uint32)):
+        bad = tuple(np.argwhere(got.view(np.uint32) != rep.view(np.uint32))[0])
+        raise AssertionError(f"{what}: differs from the FP32 replay at {bad}: {got[bad]!r} vs {rep[bad]!r}")

@@ -23,7 +23,7 @@ import torch
 import oracle
 import row_reductions_amd as lr
 import synth
-from gpu_util import ATOL, DEV, RTOL, assert_parity
+from gpu_util import ATOL, DEV, RTOL, assert_parity, bits_equal, guards_intact, placed
 
 pytestmark = pytest.mark.gpu
 
@@ -31,8 +31,6 @@ OPS = ["softmax", "rmsnorm", "layernorm", "cross_entropy", "add_layernorm", "row
 POLICIES = ["unordered_tree", "ordered_fold", "ordered_tree", "fold_right"]
 EPS = {"rmsnorm": 1e-6, "layernorm": 1e-5, "add_layernorm": 1e-5}
 CASES = 160
-GUARD = 16           # floats of guard on each side of every output
-CANARY = -1.5 * 2.0 ** 126  # guard value (exact in FP32)
 
 
 def draw(k):
@@ -81,16 +79,6 @@ def inputs(c):
     return d
 
 
-def placed(a, off):
-    """`a` (float32) on the device `off` floats past a 16-byte boundary,
-    between guard regions: (view, whole buffer)."""
-    flat = np.ascontiguousarray(a, dtype=np.float32).reshape(-1)
-    full = torch.full((flat.size + 2 * GUARD + off,), CANARY, dtype=torch.float32, device=DEV)
-    view = full[GUARD + off:GUARD + off + flat.size]
-    view.copy_(torch.from_numpy(flat).to(DEV))
-    return view.view(a.shape), full
-
-
 def choose_plan(c, aligned):
     if not c["use_plan"]:
         return None
@@ -102,12 +90,6 @@ def choose_plan(c, aligned):
 def ordered_bound(op, policy, n):
     steps = max(1, math.ceil(math.log2(n))) if policy == "ordered_tree" else max(1, n - 1)
     return steps * 2.0 ** -24 / (1 - steps * 2.0 ** -24)
-
-
-def bits_equal(got, rep, what):
-    if not np.array_equal(got.view(np.uint32), rep.view(np.uint32)):
-        bad = tuple(np.argwhere(got.view(np.uint32) != rep.view(np.uint32))[0])
-        raise AssertionError(f"{what}: differs from the FP32 replay at {bad}: {got[bad]!r} vs {rep[bad]!r}")
 
 
 @pytest.mark.parametrize("k", range(CASES))
@@ -163,10 +145,7 @@ def test_random_case(k):
     torch.cuda.synchronize()
     assert st == lr.LR_OK, lr.lr_status_string(st)
     for view, full in outs:
-        f = full.cpu().numpy()
-        n = view.numel()
-        start = view.storage_offset() - full.storage_offset()
-        assert (f[:start] == CANARY).all() and (f[start + n:] == CANARY).all(), f"case {k}: guard written"
+        assert guards_intact(view, full), f"case {k}: guard written"
     got = [v.cpu().numpy() for v, _ in outs]
     what = f"case {k} {op} {rows}x{cols} {policy}"
     gam, bet = d.get("gamma"), d.get("beta")

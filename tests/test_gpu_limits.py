@@ -9,9 +9,11 @@ so the reference replays the policy's FP32 sum over the correctly rounded
 exponentials (the device's expf is within an ulp or two of them; the sums
 then differ by a few ulp at most).
 
-A tall, narrow problem, (2^26 + 3) x 1, whose grid exceeds one dispatch
-(2^31 work-items): the call runs as several dispatches of whole workgroups of
-rows, and every row, the last piece's included, must hold its result."""
+A tall, narrow problem, (2^26 + 3) x 1: under a whole-wave plan (64 lanes per
+row) its grid exceeds one dispatch (2^31 work-items), so the call runs as
+several dispatches of whole workgroups of rows, and every row, the last
+piece's included, must hold its result.  The automatic plan (sub-wave teams,
+16 rows per wave) covers it in one dispatch."""
 import numpy as np
 import pytest
 import torch
@@ -138,26 +140,41 @@ def tall():
     return x, lab, x.cpu().numpy(), lab.cpu().numpy()
 
 
+def whole_wave_plan(op, policy):
+    """the automatic plan, or for the unordered policy (whose automatic plan
+    packs several rows per wave) the whole-wave CACHE plan with 16 rows per
+    workgroup"""
+    plan = lr.lr_plan_query(op, TALL, 1, policy)
+    if plan.lanes_per_row == 64:
+        return plan
+    facts = lr.lr_device_facts_query()
+    return next(p for p in lr.lr_plan_enumerate(facts, op, TALL, 1, policy, 0)
+                if p.family == lr.LR_FAMILY_CACHE and p.lanes_per_row == 64 and p.rows_per_block == 16)
+
+
 @pytest.mark.parametrize("op,policy", [(o, "unordered_tree") for o in
                                        ("softmax", "rmsnorm", "layernorm", "cross_entropy", "add_layernorm",
                                         "row_sum", "row_minmax")]
-                         + [("row_sum", "ordered_fold"), ("rmsnorm", "ordered_tree"), ("softmax", "fold_right")])
+                         + [("row_sum", "ordered_fold"), ("rmsnorm", "ordered_tree"), ("softmax", "fold_right"),
+                            ("softmax", "automatic"), ("layernorm", "automatic")])
 def test_tall_narrow_problem_runs_as_several_dispatches(tall, op, policy):
     x, lab, hx, hlab = tall
-    plan = lr.lr_plan_query(op, TALL, 1, policy)
+    auto = policy == "automatic"
+    policy = "unordered_tree" if auto else policy
+    plan = lr.lr_plan_query(op, TALL, 1, policy) if auto else whole_wave_plan(op, policy)
     step = lr.lr_dispatch_rows(plan, TALL)
-    print(f"\n[gpu] tall {op} {TALL}x1 {policy}: {lr.FAMILY_NAMES[plan.family]} "
+    print(f"\n[gpu] tall {op} {TALL}x1 {policy}: {lr.FAMILY_NAMES[plan.family]} lanes={plan.lanes_per_row} "
           f"Q={plan.rows_per_block}, {-(-TALL // step)} dispatches", flush=True)
-    assert step < TALL
+    assert step == TALL if auto else step < TALL
     nan = float("nan")
     if op in ("cross_entropy", "row_sum", "row_minmax"):
         o1, o2 = torch.full((TALL,), nan, device=DEV), torch.full((TALL,), nan, device=DEV)
         if op == "cross_entropy":
-            st = lr.lr_cross_entropy_f32(x, lab, o1, TALL, 1, policy)
+            st = lr.lr_cross_entropy_f32(x, lab, o1, TALL, 1, policy, plan=plan)
         elif op == "row_sum":
-            st = lr.lr_row_sum_f32(x, o1, TALL, 1, policy)
+            st = lr.lr_row_sum_f32(x, o1, TALL, 1, policy, plan=plan)
         else:
-            st = lr.lr_row_minmax_f32(x, o1, o2, TALL, 1, policy)
+            st = lr.lr_row_minmax_f32(x, o1, o2, TALL, 1, policy, plan=plan)
         torch.cuda.synchronize()
         assert st == lr.LR_OK, lr.lr_status_string(st)
         got = o1.cpu().numpy()
@@ -173,16 +190,16 @@ def test_tall_narrow_problem_runs_as_several_dispatches(tall, op, policy):
     g = torch.full((1,), 1.5, device=DEV)
     b = torch.full((1,), 0.25, device=DEV)
     if op == "softmax":
-        st = lr.lr_softmax_f32(x, y, TALL, 1, policy)
+        st = lr.lr_softmax_f32(x, y, TALL, 1, policy, plan=plan)
         ref = np.ones((TALL, 1))
     elif op == "rmsnorm":
-        st = lr.lr_rmsnorm_f32(x, g, y, TALL, 1, 1e-6, policy)
+        st = lr.lr_rmsnorm_f32(x, g, y, TALL, 1, 1e-6, policy, plan=plan)
         ref = oracle.rmsnorm(hx, np.array([1.5], np.float32), 1e-6)
     elif op == "layernorm":
-        st = lr.lr_layernorm_f32(x, g, b, y, TALL, 1, 1e-5, policy)
+        st = lr.lr_layernorm_f32(x, g, b, y, TALL, 1, 1e-5, policy, plan=plan)
         ref = np.full((TALL, 1), 0.25)  # a one-column row has zero variance: y = beta
     else:
-        st = lr.lr_add_layernorm_f32(x, x, g, b, y, None, TALL, 1, 1e-5, policy)
+        st = lr.lr_add_layernorm_f32(x, x, g, b, y, None, TALL, 1, 1e-5, policy, plan=plan)
         ref = np.full((TALL, 1), 0.25)
     torch.cuda.synchronize()
     assert st == lr.LR_OK, lr.lr_status_string(st)

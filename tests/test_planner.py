@@ -57,7 +57,14 @@ def test_plans_respect_device_limits():
         for rows, cols in [(1, 1), (37, 1537), (768, 6144), (4096, 32000), (5, 100000)]:
             for policy in POLICIES:
                 for p in lr.lr_plan_enumerate(F, op, rows, cols, policy, 1 if cols % 4 == 0 else 0):
-                    assert p.threads_per_block == 64 * p.waves_per_row * p.rows_per_block <= 1024
+                    if p.lanes_per_row < 64:  # sub-wave teams: CACHE, one wave's lanes shared by rows
+                        assert p.family == lr.LR_FAMILY_CACHE and p.waves_per_row == 1
+                        assert p.lanes_per_row in (4, 8, 16, 32) and p.rows_per_block % (64 // p.lanes_per_row) == 0
+                        assert p.threads_per_block == p.lanes_per_row * p.rows_per_block <= 1024
+                        assert p.chunks_per_lane in (1, 2)
+                    else:
+                        assert p.lanes_per_row == 64 * p.waves_per_row
+                        assert p.threads_per_block == 64 * p.waves_per_row * p.rows_per_block <= 1024
                     if p.family == lr.LR_FAMILY_SPLIT:
                         assert p.rows_per_block == 1 and 2 <= p.splits <= 64
                         assert p.blocks == rows * p.splits
@@ -297,7 +304,11 @@ def test_dispatch_rows_keep_each_dispatch_within_2_31_work_items():
                             assert (blocks + (p.splits or 1)) * p.threads_per_block > limit  # pieces are full
                         checked += 1
     assert checked > 500
-    # the grid of a tall, narrow problem does not fit one dispatch
-    p = lr.lr_plan_for_device(F, "softmax", (1 << 26) + 3, 1, "unordered_tree", 0)
-    assert lr.lr_dispatch_rows(p, (1 << 26) + 3) < (1 << 26) + 3
+    # the grid of a tall, narrow problem under a whole-wave plan does not fit
+    # one dispatch; the automatic plan packs 16 rows per wave and does
+    tall = (1 << 26) + 3
+    whole = [p for p in lr.lr_plan_enumerate(F, "softmax", tall, 1, "unordered_tree", 0) if p.lanes_per_row == 64]
+    assert whole and all(lr.lr_dispatch_rows(p, tall) < tall for p in whole)
+    p = lr.lr_plan_for_device(F, "softmax", tall, 1, "unordered_tree", 0)
+    assert p.lanes_per_row == 4 and lr.lr_dispatch_rows(p, tall) == tall
     assert lr.lr_dispatch_rows(None, 5) == 0 and lr.lr_dispatch_rows(p, 0) == 0
