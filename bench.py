@@ -318,6 +318,34 @@ def main():
             extra[name] = {"us_per_op": round(us, 3), "gbps": round(rb / us / 1e3, 1),
                            "pct_of_hbm_peak": round(100 * rb / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": rb}
         del cx
+        # narrow rows (several rows per wave): 262144 x 64, four rotating
+        # 67 MB input/output sets (537 MB, past the Infinity Cache)
+        nx = [torch.randn(262144, 64, device=dev) for _ in range(4)]
+        ny = [torch.empty_like(t) for t in nx]
+        ng, nb = torch.rand(64, device=dev) + 0.5, torch.randn(64, device=dev) * 0.1
+        for name, op, fn in (
+            ("softmax_262144x64_cold", "softmax",
+             lambda i: lr.lib.lr_softmax_f32(nx[i % 4].data_ptr(), ny[i % 4].data_ptr(), 262144, 64, 0, sh)),
+            ("layernorm_262144x64_cold", "layernorm",
+             lambda i: lr.lib.lr_layernorm_f32(nx[i % 4].data_ptr(), ng.data_ptr(), nb.data_ptr(),
+                                               ny[i % 4].data_ptr(), 262144, 64, 1e-5, 0, sh))):
+            for i in range(8):
+                lr.check(fn(i), name)
+            torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(n):
+                fn(i)
+            z.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(z) * 1e3 / n
+            nbytes = op_bytes(262144, 64)
+            p = lr.lr_plan_query(op, 262144, 64)
+            extra[name] = {"us_per_op": round(us, 3), "gbps": round(nbytes / us / 1e3, 1),
+                           "pct_of_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": nbytes,
+                           "plan": {k: v for k, v in p.as_dict().items() if k in (
+                               "family", "lanes_per_row", "rows_per_block", "chunks_per_lane", "threads_per_block")}}
+        del nx, ny
         out["extra"] = extra
 
     if args.copy_probe:

@@ -249,8 +249,13 @@ static int enumerate_all(const lr_device_facts* f, int op, int64_t rows, int64_t
 //     the gamma/beta prefetch;
 //   * cross-entropy keeps nothing after its single pass, so long rows take
 //     the STREAM family (online max / sum of exp, no register copy);
-//   * one row per workgroup, except that single-wave rows are packed four to
-//     a workgroup when rows are plentiful.
+//   * one row per workgroup (on MI355X, packing four single-wave rows per
+//     workgroup measured up to 10% slower: LayerNorm 65536 x 256, 23.7 against
+//     26.1 us);
+//   * rows of at most 32 chunks, when rows are plentiful: sub-wave teams, one
+//     chunk per lane, one wave per workgroup for 16-byte aligned rows and
+//     four for misaligned ones (softmax 262144 x 64: 22.0 against 50.8 us for
+//     whole waves; 262144 x 50: 22.3 against 24.4 us with one wave).
 // Measured winners for known shapes (lr_plan_table.inc) take precedence.
 // ---------------------------------------------------------------------------
 struct TableEntry {
@@ -344,11 +349,11 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
     }
     if (S == 1 && nv <= 32) {
         // rows plentiful and narrow: sub-wave teams with one chunk per lane
-        // (the smallest power of two lanes from 4 to 32 that covers the row),
-        // four waves per workgroup
+        // (the smallest power of two lanes from 4 to 32 that covers the row)
         int L = 4;
         while (L < nv) L *= 2;
-        lr_plan p = make_plan(LR_FAMILY_CACHE, 1, 4 * (kWave / L), 1, rows, cols, op, aligned, 0, L);
+        const int waves = aligned ? 1 : 4;
+        lr_plan p = make_plan(LR_FAMILY_CACHE, 1, waves * (kWave / L), 1, rows, cols, op, aligned, 0, L);
         if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
     }
     int family = LR_FAMILY_CACHE;
@@ -358,8 +363,7 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
         nch = kStreamUnroll;
         if (op == LR_OP_CROSS_ENTROPY) S = std::max(S, 8);
     }
-    int Q = (S == 1 && rows >= 4 * (int64_t)f->compute_units * 4) ? 4 : 1;
-    lr_plan p = make_plan(family, S, Q, nch, rows, cols, op, aligned);
+    lr_plan p = make_plan(family, S, 1, nch, rows, cols, op, aligned);
     if (validate_plan(f, op, rows, cols, policy, aligned, &p) != LR_OK)
         p = make_plan(LR_FAMILY_STREAM, S, 1, kStreamUnroll, rows, cols, op, aligned);
     return p;

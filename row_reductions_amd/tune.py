@@ -136,7 +136,8 @@ def main(argv=None):
     ap.add_argument("--eps", type=float, default=1e-5)
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough for >= 1 GB)")
     ap.add_argument("--iters", type=int, default=200)
-    ap.add_argument("--max-rows-per-block", type=int, default=4)
+    ap.add_argument("--max-rows-per-block", type=int, default=4,
+                    help="whole-wave plans: rows per workgroup; sub-wave plans: waves per workgroup")
     ap.add_argument("--json", action="store_true", help="one JSON line per candidate")
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays (launch-bound shapes)")
     ap.add_argument("--compare", nargs="+", metavar="PLAN",
@@ -185,7 +186,10 @@ def main(argv=None):
         return _compare(args, op, rows, cols, aligned, facts, auto, run, ys, ref, bound, timer, stream)
     results = []
     for p in lr.lr_plan_enumerate(facts, op, rows, cols, args.policy, aligned):
-        if p.rows_per_block > args.max_rows_per_block:
+        # whole-wave plans: at most that many rows per workgroup; sub-wave
+        # plans (several rows per wave): at most that many waves
+        packed = p.threads_per_block // 64 if p.lanes_per_row < 64 else p.rows_per_block
+        if packed > args.max_rows_per_block:
             continue
         st = run(0, p)
         torch.cuda.synchronize()
