@@ -27,10 +27,13 @@ def covered_once(plan, rows, cols, aligned):
     return True
 
 
-def make_plan(family, S, Q, vec, nch, blocks, splits):
+def make_plan(family, S, Q, vec, nch, blocks, splits, lanes=0):
+    """lanes: 4 .. 32 for a sub-wave team (lanes * Q threads), else whole waves"""
     p = lr.LrPlan()
     p.family, p.waves_per_row, p.rows_per_block, p.vec = family, S, Q, vec
-    p.chunks_per_lane, p.threads_per_block, p.blocks, p.splits = nch, 64 * S * Q, blocks, splits
+    p.chunks_per_lane, p.blocks, p.splits = nch, blocks, splits
+    p.threads_per_block = lanes * Q if lanes else 64 * S * Q
+    p.lanes_per_row = lanes if lanes else 64 * S
     return p
 
 
@@ -104,6 +107,24 @@ def test_every_enumerated_and_automatic_plan_is_accepted_and_covers(problem):
     for p in plans[:: max(1, len(plans) // 12)] + plans[-2:]:
         assert lr.lr_plan_validate(F, op, rows, cols, policy, aligned, p) == lr.LR_OK
         assert covered_once(p, rows, cols, aligned), (op, rows, cols, policy, aligned, p)
+
+
+@SETTINGS
+@given(st.sampled_from(OPS), st.integers(1, 300), st.integers(1, 300), st.booleans(), st.data())
+def test_accepted_sub_wave_plans_cover_each_element_once(op, rows, cols, want_aligned, data):
+    """sub-wave CACHE plans near the boundary of legality: team width, waves
+    per workgroup (whole or not), stripe; part-empty waves and workgroups"""
+    aligned = 1 if want_aligned and cols % 4 == 0 else 0
+    L = data.draw(st.sampled_from([4, 8, 16, 32]))
+    per_wave = 64 // L
+    Q = data.draw(st.one_of(st.integers(1, 16).map(lambda w: w * per_wave), st.integers(1, 1024 // L + 1)))
+    nv = cols // 4 if aligned else (cols + 6) // 4
+    need = -(-nv // L)
+    nch = data.draw(st.sampled_from([c for c in (1, 2, 3) if c >= need - 1] or [1]))
+    p = make_plan(lr.LR_FAMILY_CACHE, 1, Q, 4, nch, -(-rows // Q), 0, L)
+    if lr.lr_plan_validate(F, op, rows, cols, "unordered_tree", aligned, p) == lr.LR_OK:
+        assert Q % per_wave == 0 and L * Q <= 1024 and nch in (1, 2) and nch >= need
+        assert covered_once(p, rows, cols, aligned), (op, rows, cols, aligned, p)
 
 
 @SETTINGS
