@@ -190,16 +190,19 @@ float oracle_fold_right_f32(const float* x, int64_t n, int kind) {
 }
 
 /* ordered_tree (reading used: the pairwise tree in index order).  The row's
- * contributions c_0 .. c_{n-1} are padded with the add identity +0.0f to the
- * next power of two; each level adds adjacent pairs, node 2i + node 2i+1,
- * until one value is left.  Every addition is one FP32 rounding. */
+ * contributions c_0 .. c_{n-1} are padded with the add identity to the next
+ * power of two; each level adds adjacent pairs, node 2i + node 2i+1, until
+ * one value is left.  Every addition is one FP32 rounding.  The identity is
+ * -0.0f, IEEE 754's exact one: x + (-0) = x for every x, whereas -0 + (+0)
+ * rounds to +0, so with -0 padding a tree padded further (to any larger
+ * power of two) gives the same bits, and a sum of negative zeros stays -0. */
 float oracle_tree_f32(const float* x, int64_t n, int kind) {
     int64_t p = 1;
     while (p < n) p *= 2;
     float* t = (float*)malloc((size_t)p * sizeof(float));
     if (t == NULL) return NAN;
     for (int64_t j = 0; j < p; ++j) {
-        float c = 0.0f;
+        float c = -0.0f;
         if (j < n) c = (kind == 1) ? x[j] * x[j] : x[j];
         t[j] = c;
     }

@@ -512,9 +512,10 @@ def test_tree_zero_padding_and_halves():
         p = 1
         while p < n:
             p *= 2
-        # padding with +0 up to the tree's own width, or beyond, changes nothing
+        # padding with -0 (the add identity) up to the tree's own width, or
+        # beyond, changes nothing
         for extra in (p - n, 2 * p - n, 4 * p - n):
-            xp = np.concatenate([x, np.zeros(extra, np.float32)])
+            xp = np.concatenate([x, np.full(extra, -0.0, np.float32)])
             assert oracle.ordered_sum_f32(xp, "ordered_tree") == oracle.ordered_sum_f32(x, "ordered_tree")
     # a full tree is the rounded sum of its two half trees
     for k in range(1, 12):
@@ -524,6 +525,25 @@ def test_tree_zero_padding_and_halves():
         halves = np.float32(np.float32(oracle.ordered_sum_f32(x[:h], "ordered_tree")) +
                             np.float32(oracle.ordered_sum_f32(x[h:], "ordered_tree")))
         assert np.float32(whole) == halves
+
+
+def test_tree_of_negative_zeros_is_negative_zero():
+    """IEEE 754 (section 6.3): a sum of negative zeros is -0, and -0 is the
+    exact add identity (x + -0 == x, sign included).  A tree padded with +0
+    instead would turn a row of negative zeros into +0 whenever it pads; so
+    would padding a power-of-two row any further."""
+    for n in (1, 2, 3, 4, 5, 64, 100, 256, 257):
+        x = np.full(n, -0.0, np.float32)
+        t = np.float32(oracle.ordered_sum_f32(x, "ordered_tree"))
+        assert t == 0.0 and math.copysign(1.0, t) == -1.0, n
+        # one +0 anywhere makes the exact sum +0
+        x[n // 2] = 0.0
+        t = np.float32(oracle.ordered_sum_f32(x, "ordered_tree"))
+        assert t == 0.0 and math.copysign(1.0, t) == 1.0, n
+    # the padding keeps every value's sign and bits, zeros included
+    for v in (-0.0, 0.0, -1.5, 3.0e-45):
+        x = np.array([v, -0.0, -0.0], np.float32)
+        assert np.float32(oracle.ordered_sum_f32(x, "ordered_tree")).view(np.uint32) == np.float32(v).view(np.uint32)
 
 
 def test_tree_leaf_pairs_commute_but_left_fold_does_not():
