@@ -5,7 +5,9 @@
 //   fold_right: the same chain taken from the right end, acc = c_j + acc,
 //       j = cols-1 .. 0;
 //   ordered_tree: the pairwise tree in index order over the contributions
-//       padded with +0.0f to the next power of two.
+//       padded with the add identity -0.0f to the next power of two (x + -0
+//       is x for every x, so padding further, as the 256-leaf slabs do,
+//       changes no bit).
 // Each multiply and add is rounded on its own; division and square root are
 // IEEE (built with -ffp-contract=off and correctly rounded divide/sqrt); max
 // and min folds are exact and use the wave tree.  The result does not depend
@@ -22,7 +24,7 @@
 // slab sums are then merged like a binary counter on a small LDS stack (two
 // adjacent complete subtrees of equal size merge at once), and the partial
 // subtrees left at the end are added from the smallest up, which is the tree
-// over the zero-padded row.
+// over the padded row.
 #pragma clang fp contract(off)
 
 #include "lr_device.hpp"
@@ -181,8 +183,8 @@ __device__ __forceinline__ float ordered_sum(const float* xr, const float* rr, i
 #pragma unroll
         for (int i = 0; i < kSlab / kWave; ++i) {
             const int e = ordered_elem(slab_id, i, lane);
-            // past the row: the add identity (the tree's padding; never read by the folds)
-            slab[kWave * i + lane] = e < cols ? contrib<C>(buf[i], ref) : 0.0f;
+            // past the row: the add identity -0 (the tree's padding; never read by the folds)
+            slab[kWave * i + lane] = e < cols ? contrib<C>(buf[i], ref) : -0.0f;
         }
         wave_sync();
         fetch(refill < nslab ? slab_of(refill) : nslab, buf);  // past the last slab: zeros, no traffic
@@ -230,7 +232,7 @@ __device__ __forceinline__ float ordered_sum(const float* xr, const float* rr, i
     if (t < nslab) step(t, bufa, t + 2);
     if constexpr (POL == kPolTree) {
         // partial subtrees, largest first: add from the smallest up (each one's
-        // missing right sibling is all padding, an exact +0)
+        // missing right sibling is all padding, -0, whose addition is exact)
         acc = stk[depth - 1];
         for (int k = depth - 2; k >= 0; --k) acc = stk[k] + acc;
     }

@@ -144,9 +144,13 @@ lr_status validate_plan(const lr_device_facts* f, int op, int64_t rows, int64_t 
     const int S = p->waves_per_row, Q = p->rows_per_block, L = p->lanes_per_row;
     if (!family_allowed(policy, p->family)) return LR_ERR_UNREALIZABLE_PLAN;
     if (narrow_lanes(L)) {
-        // sub-wave teams: CACHE only, one team per L lanes, whole waves per
-        // workgroup, a compiled stripe that covers the widest row
-        if (p->family != LR_FAMILY_CACHE || S != 1 || Q < 1 || Q % (kWave / L) != 0) return LR_ERR_UNREALIZABLE_PLAN;
+        // sub-wave teams: CACHE, or TREE with one chunk per lane on aligned
+        // rows; one team per L lanes, whole waves per workgroup, a compiled
+        // stripe that covers the widest row
+        const bool tree = p->family == LR_FAMILY_TREE;
+        if ((p->family != LR_FAMILY_CACHE && !tree) || S != 1 || Q < 1 || Q % (kWave / L) != 0)
+            return LR_ERR_UNREALIZABLE_PLAN;
+        if (tree && (!aligned || p->chunks_per_lane != 1)) return LR_ERR_UNREALIZABLE_PLAN;
         if ((int64_t)L * Q > f->max_threads_per_block || p->threads_per_block != L * Q) return LR_ERR_UNREALIZABLE_PLAN;
         if (p->splits != 0 || p->blocks != (rows + Q - 1) / Q || p->blocks > INT32_MAX) return LR_ERR_UNREALIZABLE_PLAN;
         if (p->vec != kVec || !narrow_chunks_compiled(p->chunks_per_lane)) return LR_ERR_UNREALIZABLE_PLAN;
@@ -209,6 +213,11 @@ static int enumerate_all(const lr_device_facts* f, int op, int64_t rows, int64_t
                 if (nch == 0) continue;
                 for (int Q = 1; S * Q <= kMaxWaves; ++Q)
                     push(make_plan(LR_FAMILY_TREE, S, Q, nch, rows, cols, op, aligned));
+            }
+            for (int L : kNarrowLanes) {  // sub-wave teams, one chunk per lane
+                if (nv > L) continue;
+                for (int w = 1; w <= kMaxWaves; ++w)
+                    push(make_plan(LR_FAMILY_TREE, 1, w * (kWave / L), 1, rows, cols, op, aligned, 0, L));
             }
         }
         for (int Q = 1; Q <= kMaxWaves; ++Q) push(make_plan(LR_FAMILY_ORDERED, 1, Q, 0, rows, cols, op, aligned));
@@ -340,7 +349,14 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
     while (S < kMaxWaves && need(S) > 8) ++S;
     if (policy != LR_UNORDERED_TREE) {
         // ordered_tree on aligned rows: the cache layout with the tree combine
+        // (sub-wave teams for narrow rows, as for the unordered policy)
         if (policy == LR_ORDERED_TREE) {
+            if (S == 1 && nv <= 32) {
+                int L = 4;
+                while (L < nv) L *= 2;
+                lr_plan p = make_plan(LR_FAMILY_TREE, 1, kWave / L, 1, rows, cols, op, aligned, 0, L);
+                if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
+            }
             lr_plan p = make_plan(LR_FAMILY_TREE, S, 1, smallest_cache_instance(need(S)), rows, cols, op, aligned);
             if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
         }
@@ -440,7 +456,8 @@ extern "C" lr_status lr_coverage_check(const lr_plan* p, int64_t rows, int64_t c
     const int S = p->waves_per_row, Q = p->rows_per_block, L = p->lanes_per_row;
     const bool narrow = narrow_lanes(L);
     if (S < 1 || Q < 1 || p->threads_per_block != (narrow ? L * Q : kWave * S * Q)) return LR_ERR_UNREALIZABLE_PLAN;
-    if (narrow && (p->family != LR_FAMILY_CACHE || S != 1)) return LR_ERR_UNREALIZABLE_PLAN;
+    if (narrow && ((p->family != LR_FAMILY_CACHE && p->family != LR_FAMILY_TREE) || S != 1))
+        return LR_ERR_UNREALIZABLE_PLAN;
     const int c = (int)cols;
     if (p->family == LR_FAMILY_SPLIT && (p->splits < 1 || Q != 1)) return LR_ERR_UNREALIZABLE_PLAN;
     for (int64_t b = 0; b < p->blocks; ++b) {

@@ -120,3 +120,109 @@ def test_prior_packs_narrow_rows():
     assert lr.lr_plan_for_device(facts, "softmax", 37, 64, "unordered_tree", 1).lanes_per_row == 64 * \
         lr.lr_plan_for_device(facts, "softmax", 37, 64, "unordered_tree", 1).waves_per_row
     assert lr.lr_plan_for_device(facts, "softmax", 262144, 512, "unordered_tree", 1).lanes_per_row == 64
+
+
+TREE_COLS = [4, 8, 16, 32, 64, 100, 128]  # aligned rows (TREE plans need them)
+
+
+def replay_ok(op, d, got, what, y2=None):
+    """ordered_tree gate: bit-equal FP32 replays (norms, sums), the widened
+    bar for softmax / cross-entropy, exact min / max"""
+    import math
+    x = d["x"]
+    pol = "ordered_tree"
+    if op == "rmsnorm":
+        rep = oracle.rmsnorm_ordered_f32(x, d["gamma"], EPS[op], pol)
+    elif op == "layernorm":
+        rep = oracle.layernorm_ordered_f32(x, d["gamma"], d["beta"], EPS[op], pol)
+    elif op == "add_layernorm":
+        _, comb = oracle.add_layernorm(x, d["residual"], None, None, EPS[op], with_sum=True)
+        rep = oracle.layernorm_ordered_f32(comb, d["gamma"], d["beta"], EPS[op], pol)
+    elif op == "row_sum":
+        rep = np.array([oracle.ordered_sum_f32(r, pol) for r in x], dtype=np.float32)
+    elif op == "row_minmax":
+        lo, hi = oracle.row_minmax(x)
+        assert np.array_equal(got, lo) and np.array_equal(y2, hi), what
+        return
+    else:
+        n = x.shape[1]
+        steps = max(1, math.ceil(math.log2(n)))
+        g = steps * 2.0 ** -24 / (1 - steps * 2.0 ** -24)
+        ref = oracle.softmax(x) if op == "softmax" else oracle.cross_entropy(x, d["labels"])
+        err = np.abs(got.astype(np.float64) - ref)
+        bound = ATOL + (RTOL + g) * np.abs(ref) + (g if op == "cross_entropy" else 0.0)
+        assert (err <= bound).all(), f"{what}: worst err/bound {(err / bound).max():.3g}"
+        return
+    assert np.array_equal(got.view(np.uint32), rep.view(np.uint32)), what
+
+
+@pytest.mark.parametrize("cols", TREE_COLS)
+@pytest.mark.parametrize("op", OPS)
+def test_sub_wave_tree_teams(op, cols):
+    """ordered_tree on sub-wave teams (one chunk per lane): the FP32 tree over
+    the row, bit for bit, whatever the team width"""
+    d = inputs(op, cols, seed=100 + cols)
+    x = d["x"]
+    facts = lr.lr_device_facts_query()
+    plans = [p for p in lr.lr_plan_enumerate(facts, op, ROWS, cols, "ordered_tree", 1)
+             if p.family == lr.LR_FAMILY_TREE and p.lanes_per_row < 64 and p.threads_per_block in (64, 256)]
+    assert plans
+    g = torch.from_numpy(d["gamma"]).to(DEV)
+    b = torch.from_numpy(d["beta"]).to(DEV)
+    for plan in plans:
+        print(f"\n[gpu] narrow tree {op} {ROWS}x{cols} lanes={plan.lanes_per_row} Q={plan.rows_per_block}", flush=True)
+        xv = torch.from_numpy(x).to(DEV)
+        what = f"{op} {ROWS}x{cols} ordered_tree {plan}"
+        y2 = None
+        if op in ("cross_entropy", "row_sum", "row_minmax"):
+            o1, o2 = torch.empty(ROWS, device=DEV), torch.empty(ROWS, device=DEV)
+            if op == "cross_entropy":
+                st = lr.lr_cross_entropy_f32(xv, torch.from_numpy(d["labels"]).to(DEV), o1, ROWS, cols,
+                                             "ordered_tree", plan=plan)
+            elif op == "row_sum":
+                st = lr.lr_row_sum_f32(xv, o1, ROWS, cols, "ordered_tree", plan=plan)
+            else:
+                st = lr.lr_row_minmax_f32(xv, o1, o2, ROWS, cols, "ordered_tree", plan=plan)
+                y2 = o2
+            out = o1
+        else:
+            out = torch.empty_like(xv)
+            if op == "softmax":
+                st = lr.lr_softmax_f32(xv, out, ROWS, cols, "ordered_tree", plan=plan)
+            elif op == "rmsnorm":
+                st = lr.lr_rmsnorm_f32(xv, g, out, ROWS, cols, EPS[op], "ordered_tree", plan=plan)
+            elif op == "layernorm":
+                st = lr.lr_layernorm_f32(xv, g, b, out, ROWS, cols, EPS[op], "ordered_tree", plan=plan)
+            else:
+                rv = torch.from_numpy(d["residual"]).to(DEV)
+                st = lr.lr_add_layernorm_f32(xv, rv, g, b, out, None, ROWS, cols, EPS[op], "ordered_tree", plan=plan)
+        torch.cuda.synchronize()
+        assert st == lr.LR_OK, lr.lr_status_string(st)
+        replay_ok(op, d, out.cpu().numpy(), what, None if y2 is None else y2.cpu().numpy())
+
+
+@pytest.mark.parametrize("cols", [4, 64, 100, 256, 300, 1024])
+def test_negative_zero_rows_under_ordered_policies(cols):
+    """rows of -0.0 (and rows of -0.0 with one +0.0) under every ordered policy
+    on every plan family: a tree pads with the exact add identity -0, so its
+    sum of negative zeros is -0 at every width and on every plan; a fold
+    starts from +0 and gives +0; both equal the FP32 replays bit for bit."""
+    rows = 6
+    x = np.full((rows, cols), -0.0, np.float32)
+    x[1::2, cols // 3] = 0.0
+    facts = lr.lr_device_facts_query()
+    xv = torch.from_numpy(x).to(DEV)
+    neg = np.uint32(0x80000000)
+    for pol in ("ordered_tree", "ordered_fold", "fold_right"):
+        rep = np.array([oracle.ordered_sum_f32(r, pol) for r in x], dtype=np.float32)
+        # the tree keeps -0 for the all-negative-zero rows; a fold from +0 gives +0
+        want = np.where(np.arange(rows) % 2 == 0, neg if pol == "ordered_tree" else np.uint32(0), np.uint32(0))
+        assert np.array_equal(rep.view(np.uint32), want.astype(np.uint32)), (pol, rep)
+        for aligned in ((1, 0) if cols % 4 == 0 else (0,)):
+            for plan in lr.lr_plan_enumerate(facts, "row_sum", rows, cols, pol, aligned):
+                out = torch.full((rows,), 7.0, device=DEV)
+                st = lr.lr_row_sum_f32(xv, out, rows, cols, pol, plan=plan)
+                torch.cuda.synchronize()
+                assert st == lr.LR_OK
+                got = out.cpu().numpy()
+                assert np.array_equal(got.view(np.uint32), rep.view(np.uint32)), (pol, cols, plan, got, rep)

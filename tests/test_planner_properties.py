@@ -115,15 +115,18 @@ def test_accepted_sub_wave_plans_cover_each_element_once(op, rows, cols, want_al
     """sub-wave CACHE plans near the boundary of legality: team width, waves
     per workgroup (whole or not), stripe; part-empty waves and workgroups"""
     aligned = 1 if want_aligned and cols % 4 == 0 else 0
+    tree = data.draw(st.booleans())  # TREE plans (ordered_tree) or CACHE (unordered)
+    family, policy = (lr.LR_FAMILY_TREE, "ordered_tree") if tree else (lr.LR_FAMILY_CACHE, "unordered_tree")
     L = data.draw(st.sampled_from([4, 8, 16, 32]))
     per_wave = 64 // L
     Q = data.draw(st.one_of(st.integers(1, 16).map(lambda w: w * per_wave), st.integers(1, 1024 // L + 1)))
     nv = cols // 4 if aligned else (cols + 6) // 4
     need = -(-nv // L)
     nch = data.draw(st.sampled_from([c for c in (1, 2, 3) if c >= need - 1] or [1]))
-    p = make_plan(lr.LR_FAMILY_CACHE, 1, Q, 4, nch, -(-rows // Q), 0, L)
-    if lr.lr_plan_validate(F, op, rows, cols, "unordered_tree", aligned, p) == lr.LR_OK:
+    p = make_plan(family, 1, Q, 4, nch, -(-rows // Q), 0, L)
+    if lr.lr_plan_validate(F, op, rows, cols, policy, aligned, p) == lr.LR_OK:
         assert Q % per_wave == 0 and L * Q <= 1024 and nch in (1, 2) and nch >= need
+        assert not tree or (aligned and nch == 1)
         assert covered_once(p, rows, cols, aligned), (op, rows, cols, aligned, p)
 
 
