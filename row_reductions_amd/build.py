@@ -35,7 +35,7 @@ COMMON = [
 # operation on its own and use IEEE division and square root.
 ORDERED_FLAGS = ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt"]
 TREE_OPS = ["softmax", "cross_entropy", "rmsnorm", "layernorm", "add_layernorm", "row_sum", "row_minmax"]
-EXTRA = {"k_ordered.hip": ORDERED_FLAGS}
+EXTRA = {"k_ordered.hip": ORDERED_FLAGS, "k_ordered_lane.hip": ORDERED_FLAGS}
 EXTRA.update({f"k_tree_{op}.hip": ORDERED_FLAGS for op in TREE_OPS})
 
 SOURCES = [
@@ -49,6 +49,7 @@ SOURCES = [
     "k_row_sum.hip",
     "k_row_minmax.hip",
     "k_ordered.hip",
+    "k_ordered_lane.hip",
     *[f"k_tree_{op}.hip" for op in TREE_OPS],
 ]
 

@@ -152,7 +152,10 @@ lr_status validate_call(const Call& c) {
 }
 
 hipError_t launch_piece(int op, int policy, const KArgs& a, const lr_plan& plan, bool aligned, hipStream_t stream) {
-    if (plan.family == LR_FAMILY_ORDERED) return launch_ordered(op, policy, a, plan, stream);
+    if (plan.family == LR_FAMILY_ORDERED) {
+        return plan.lanes_per_row == 1 ? launch_ordered_lane(op, policy, a, plan, aligned, stream)
+                                       : launch_ordered(op, policy, a, plan, stream);
+    }
     if (plan.family == LR_FAMILY_TREE) {
         switch (op) {
             case LR_OP_SOFTMAX: return launch_tree_softmax(a, plan, aligned, stream);

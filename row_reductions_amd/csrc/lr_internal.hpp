@@ -40,6 +40,9 @@ struct KArgs {
 constexpr int kCacheChunks[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
 constexpr int kNumCacheChunks = sizeof(kCacheChunks) / sizeof(kCacheChunks[0]);
 constexpr int kStreamUnroll = 4;
+// Chunk counts (whole rows) of the one-lane-per-row ORDERED instances, ascending.
+constexpr int kLaneChunks[] = {1, 2, 4, 8, 16};
+constexpr int kNumLaneChunks = sizeof(kLaneChunks) / sizeof(kLaneChunks[0]);
 // Chunk counts of the sub-wave CACHE instances (lanes_per_row 4 .. 32), ascending.
 constexpr int kNarrowChunks[] = {1, 2};
 constexpr int kNumNarrowChunks = sizeof(kNarrowChunks) / sizeof(kNarrowChunks[0]);
@@ -79,6 +82,9 @@ hipError_t launch_add_layernorm(const KArgs& a, const lr_plan& p, bool aligned, 
 hipError_t launch_row_sum(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_row_minmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_ordered(int op, int policy, const KArgs& a, const lr_plan& p, hipStream_t s);
+// The ordered policies with one lane per row (lanes_per_row = 1, narrow
+// aligned rows); `aligned`: every row pointer is 16-byte aligned.
+hipError_t launch_ordered_lane(int op, int policy, const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 // TREE family (ordered_tree on the cache layout), one translation unit per op.
 hipError_t launch_tree_softmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_tree_cross_entropy(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);

@@ -226,3 +226,74 @@ def test_negative_zero_rows_under_ordered_policies(cols):
                 assert st == lr.LR_OK
                 got = out.cpu().numpy()
                 assert np.array_equal(got.view(np.uint32), rep.view(np.uint32)), (pol, cols, plan, got, rep)
+
+
+LANE_COLS = [4, 8, 20, 32, 48, 64]
+
+
+def run_op(op, d, cols, policy, plan, rows=ROWS):
+    """one call; returns the output rows (and the maxima for row_minmax)"""
+    x = torch.from_numpy(d["x"]).to(DEV)
+    g, b = torch.from_numpy(d["gamma"]).to(DEV), torch.from_numpy(d["beta"]).to(DEV)
+    if op in ("cross_entropy", "row_sum", "row_minmax"):
+        o1, o2 = torch.empty(rows, device=DEV), torch.empty(rows, device=DEV)
+        if op == "cross_entropy":
+            st = lr.lr_cross_entropy_f32(x, torch.from_numpy(d["labels"]).to(DEV), o1, rows, cols, policy, plan=plan)
+        elif op == "row_sum":
+            st = lr.lr_row_sum_f32(x, o1, rows, cols, policy, plan=plan)
+        else:
+            st = lr.lr_row_minmax_f32(x, o1, o2, rows, cols, policy, plan=plan)
+        torch.cuda.synchronize()
+        assert st == lr.LR_OK, lr.lr_status_string(st)
+        return o1.cpu().numpy(), o2.cpu().numpy()
+    y = torch.empty_like(x)
+    if op == "softmax":
+        st = lr.lr_softmax_f32(x, y, rows, cols, policy, plan=plan)
+    elif op == "rmsnorm":
+        st = lr.lr_rmsnorm_f32(x, g, y, rows, cols, EPS[op], policy, plan=plan)
+    elif op == "layernorm":
+        st = lr.lr_layernorm_f32(x, g, b, y, rows, cols, EPS[op], policy, plan=plan)
+    else:
+        st = lr.lr_add_layernorm_f32(x, torch.from_numpy(d["residual"]).to(DEV), g, b, y, None, rows, cols, EPS[op],
+                                     policy, plan=plan)
+    torch.cuda.synchronize()
+    assert st == lr.LR_OK, lr.lr_status_string(st)
+    return y.cpu().numpy(), None
+
+
+@pytest.mark.parametrize("cols", LANE_COLS)
+@pytest.mark.parametrize("op", OPS)
+def test_one_lane_per_row_ordered(op, cols):
+    """the ordered policies with one lane per row (narrow aligned rows): the
+    FP32 replays bit for bit (norms, sums), the widened bar (softmax,
+    cross-entropy), exact min / max, and every output bit-identical to the
+    one-wave-per-row plan's: the same order and the same functions"""
+    d = inputs(op, cols, seed=200 + cols)
+    facts = lr.lr_device_facts_query()
+    for policy in ("ordered_fold", "fold_right", "ordered_tree"):
+        plans = lr.lr_plan_enumerate(facts, op, ROWS, cols, policy, 1)
+        lanes = [p for p in plans if p.lanes_per_row == 1]
+        wave = next(p for p in plans if p.family == lr.LR_FAMILY_ORDERED and p.lanes_per_row == 64)
+        assert lanes, (op, cols, policy)
+        ref1, ref2 = run_op(op, d, cols, policy, wave)
+        for plan in lanes:
+            print(f"\n[gpu] lane rows {op} {ROWS}x{cols} {policy} Q={plan.rows_per_block}", flush=True)
+            got1, got2 = run_op(op, d, cols, policy, plan)
+            what = f"{op} {ROWS}x{cols} {policy} {plan}"
+            assert np.array_equal(got1.view(np.uint32), ref1.view(np.uint32)), what + " vs the wave plan"
+            if got2 is not None:
+                assert np.array_equal(got2.view(np.uint32), ref2.view(np.uint32)), what
+            if policy == "ordered_tree":
+                replay_ok(op, d, got1, what, got2)
+            elif op in ("rmsnorm", "layernorm", "add_layernorm", "row_sum"):
+                x = d["x"]
+                if op == "rmsnorm":
+                    rep = oracle.rmsnorm_ordered_f32(x, d["gamma"], EPS[op], policy)
+                elif op == "layernorm":
+                    rep = oracle.layernorm_ordered_f32(x, d["gamma"], d["beta"], EPS[op], policy)
+                elif op == "add_layernorm":
+                    _, comb = oracle.add_layernorm(x, d["residual"], None, None, EPS[op], with_sum=True)
+                    rep = oracle.layernorm_ordered_f32(comb, d["gamma"], d["beta"], EPS[op], policy)
+                else:
+                    rep = np.array([oracle.ordered_sum_f32(r, policy) for r in x], dtype=np.float32)
+                assert np.array_equal(got1.view(np.uint32), rep.view(np.uint32)), what
