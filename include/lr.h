@@ -60,8 +60,9 @@ typedef struct ihipStream_t* hipStream_t;
  *                      exp/log/rcp/rsqrt; repeatable for a fixed plan.
  *   LR_ORDERED_FOLD    fold_left: one FP32 chain j = 0 .. cols-1 from +0.0f.
  *   LR_ORDERED_TREE    the pairwise tree in index order over the row's
- *                      contributions padded with +0.0f to the next power of
- *                      two (adjacent pairs added level by level).
+ *                      contributions padded with -0.0f (the exact add
+ *                      identity) to the next power of two (adjacent pairs
+ *                      added level by level).
  *   LR_FOLD_RIGHT      one FP32 chain j = cols-1 .. 0 from +0.0f
  *                      (acc = c_j + acc).
  * Under the three ordered policies every operation is rounded on its own (no

@@ -81,7 +81,7 @@ float oracle_fold_left_f32(const float* x, int64_t n, int kind);
 /* The other ordered policies of section 1 ("fold_right", "ordered_tree"):
  * fold_right takes the chain from the right end (acc = c_j + acc,
  * j = n-1 .. 0, from +0.0f).  ordered_tree (reading: the pairwise tree in
- * index order) pads the contributions with +0.0f to the next power of two
+ * index order) pads the contributions with -0.0f (the exact add identity) to the next power of two
  * and adds adjacent pairs level by level.  Both round every operation. */
 float oracle_fold_right_f32(const float* x, int64_t n, int kind);
 float oracle_tree_f32(const float* x, int64_t n, int kind);

@@ -3,7 +3,7 @@ reduction lowering", section 1: each reduction carries its ReductionPolicy;
 an ordered tree or fold stays ordered).
 
 ordered_tree is the pairwise tree in index order over the contributions
-padded with +0.0f to the next power of two; fold_right is the FP32 chain from
+padded with -0.0f to the next power of two; fold_right is the FP32 chain from
 the right end.  RMSNorm, LayerNorm, the fused residual LayerNorm and the row
 sum have exactly one FP32 result under each: the GPU must equal the CPU FP32
 replay (oracle) bit for bit, under every legal plan -- TREE-family plans
