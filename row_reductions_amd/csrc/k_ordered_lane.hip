@@ -2,15 +2,15 @@
 // ordered reduction policies of "TIRx Metal reduction lowering", section 1,
 // exactly as in k_ordered.hip -- fold_left and fold_right from +0.0f, the
 // pairwise tree in index order over the contributions padded with the add
-// identity -0.0f -- but with each lane owning one whole row.  Lane l of a
-// workgroup of Q lanes takes row blockIdx.x * Q + l and keeps it in
-// registers (N4 16-byte chunks, cols <= 4 N4, the row 16-byte aligned), so
-// every ordered sum is that lane's own chain or tree over its registers and
-// the elementwise passes read registers: 64 rows progress per wave, with no
-// LDS and no cross-lane operation.  A row wider than a few chunks is better
-// served by a wave (k_ordered.hip).  Same operation sequence as k_ordered.hip
-// (each multiply and add rounded on its own, IEEE division and square root,
-// precise expf / logf), so the results are the same bits.
+// identity -0.0f -- but with each lane owning one whole row.  A workgroup is
+// one wavefront; lane l takes row 64 blockIdx.x + l and keeps it in registers
+// (cols <= 4 N4 <= 64), so every ordered sum is that lane's own chain or tree
+// over its registers and the elementwise passes read registers: 64 rows
+// progress per wave, with no cross-lane arithmetic.  The rows come in and go
+// out through an LDS tile with coalesced accesses (below).  Same operation
+// sequence as k_ordered.hip (each multiply and add rounded on its own, IEEE
+// division and square root, precise expf / logf), so the results are the
+// same bits.
 #pragma clang fp contract(off)
 
 #include "lr_device.hpp"
@@ -49,60 +49,78 @@ __device__ __forceinline__ float lane_sum(const float (&c)[N], int cols) {
     }
 }
 
-// Row r's chunk c (16 bytes) read as four floats: one 128-bit access when
-// the pointer's rows are 16-byte aligned (AL), else four.
-template <bool AL>
-__device__ __forceinline__ float4 chunk_ld(const float* p, int c, bool cached) {
-    if constexpr (AL) {
-        return cached ? ld4_cached(reinterpret_cast<const float4*>(p) + c) : ld4(reinterpret_cast<const float4*>(p) + c);
-    } else {
-        return make_float4(p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]);
-    }
+// Wave-local ordering point for the LDS tile: this wave's LDS accesses
+// before it complete before any after it.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool AL>
-__device__ __forceinline__ void chunk_st(float* p, int c, float4 v) {
-    if constexpr (AL) {
-        st4(reinterpret_cast<float4*>(p) + c, v);
-    } else {
-        p[4 * c] = v.x;
-        p[4 * c + 1] = v.y;
-        p[4 * c + 2] = v.z;
-        p[4 * c + 3] = v.w;
-    }
-}
-
-// AL: y, gamma, beta, the residual and the combined output are 16-byte
-// aligned too (x always is: the plan requires it).
-template <int OP, int POL, int N4, bool AL>
-__global__ void __launch_bounds__(256) k_ordered_lane(const KArgs a) {
-    constexpr int N = 4 * N4;
-    const int64_t row = (int64_t)blockIdx.x * a.Q + threadIdx.x;
-    if (row >= a.rows) return;  // no barrier and no cross-lane operation in this kernel
+// Each wavefront owns 64 consecutive rows, which sit in memory as one block
+// of 64 * cols floats.  The block is copied through an LDS tile with
+// coalesced 32-bit accesses (flat element f = lane + 64 i goes to tile row
+// f / cols, column f % cols); the tile's row pitch is odd, so that the 64
+// lanes reading one element of their own rows hit distinct banks.  Any row
+// alignment works, and the rows past the tensor's end are read as zeros and
+// never written (the buffer resources cover the existing rows only).
+template <int OP, int POL, int N4>
+__global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
+    constexpr int N = 4 * N4;       // cols <= N
+    constexpr int PMAX = N + 1;     // odd pitch >= cols
+    __shared__ float tile[kWave * PMAX];
+    const int lane = (int)threadIdx.x;
     const int cols = a.cols;
-    const int nv = cols / kVec;  // whole chunks: cols % 4 == 0
+    const int pitch = cols | 1;
+    const int64_t r0 = (int64_t)blockIdx.x * kWave;  // the wave's first row
+    const int64_t left = a.rows - r0;
+    const int nr = left < kWave ? (int)left : kWave;  // its rows that exist (>= 1)
+    const int64_t off0 = r0 * (int64_t)cols;
+    const int nflat = nr * cols;
     const float n = (float)cols;
-    const int64_t roff = row * (int64_t)cols;
-    const float* xr = a.x + roff;
+    const int64_t row = r0 + lane;
+    const bool active = lane < nr;
 
-    // the row (x + residual for the fused residual LayerNorm), in registers
-    float x[N];
+    // flat element f -> (tile row, column), with the quotient from the FP32
+    // reciprocal corrected to the exact one (f < 64 * cols <= 2^12)
+    auto place = [&](int f) {
+        int r = (int)((float)f * a.inv_cols);
+        if (r * cols > f) --r;
+        if ((r + 1) * cols <= f) ++r;
+        return r * pitch + (f - r * cols);
+    };
+    auto copy_in = [&](const float* src, const float* add) {
+        const BufRes rs = make_res(src + off0, nflat * 4);
+        const BufRes ra = make_res(add ? add + off0 : nullptr, add ? nflat * 4 : 0);
 #pragma unroll
-    for (int c = 0; c < N4; ++c) {
-        float4 q = splat4(0.0f);
-        if (c < nv) {
-            q = chunk_ld<true>(xr, c, false);
-            if constexpr (OP == kAddLayerNorm) {
-                const float4 r = chunk_ld<AL>(a.residual + roff, c, false);
-                q = make_float4(q.x + r.x, q.y + r.y, q.z + r.z, q.w + r.w);
-                if (a.sum_out != nullptr) chunk_st<AL>(a.sum_out + roff, c, q);
+        for (int i = 0; i < N; ++i) {
+            const int f = lane + kWave * i;
+            if (i < cols) {
+                float v = res_ld1(rs, f * 4);
+                if (add) v = v + res_ld1(ra, f * 4);
+                tile[place(f)] = v;
             }
         }
-        x[4 * c] = q.x;
-        x[4 * c + 1] = q.y;
-        x[4 * c + 2] = q.z;
-        x[4 * c + 3] = q.w;
+    };
+    auto copy_out = [&](float* dst) {
+        const BufRes rd = make_res(dst + off0, nflat * 4);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int f = lane + kWave * i;
+            if (i < cols) res_st1(rd, f * 4, tile[place(f)]);
+        }
+    };
+
+    // the rows (x + residual for the fused residual LayerNorm, in FP32)
+    copy_in(a.x, OP == kAddLayerNorm ? a.residual : nullptr);
+    wave_sync();
+    if constexpr (OP == kAddLayerNorm) {
+        if (a.sum_out != nullptr) copy_out(a.sum_out);
     }
+    float x[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) x[j] = j < cols ? tile[lane * pitch + j] : 0.0f;
+    wave_sync();  // every lane has its row before any lane writes the tile
 
     if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
         float m = -INFINITY;
@@ -114,18 +132,21 @@ __global__ void __launch_bounds__(256) k_ordered_lane(const KArgs a) {
         for (int j = 0; j < N; ++j) e[j] = j < cols ? expf(x[j] - m) : 0.0f;
         const float s = lane_sum<POL>(e, cols);
         if constexpr (OP == kCrossEntropy) {
-            const int64_t lab = a.labels[row];
-            const float sel = (lab >= 0 && lab < (int64_t)cols) ? xr[lab] : 0.0f;
-            a.losses[row] = logf(s) + (m - sel);
+            if (active) {
+                const int64_t lab = a.labels[row];
+                const float sel = (lab >= 0 && lab < (int64_t)cols) ? a.x[row * (int64_t)cols + lab] : 0.0f;
+                a.losses[row] = logf(s) + (m - sel);
+            }
         } else {
 #pragma unroll
-            for (int c = 0; c < N4; ++c)
-                if (c < nv)
-                    chunk_st<AL>(a.y + roff, c,
-                                 make_float4(e[4 * c] / s, e[4 * c + 1] / s, e[4 * c + 2] / s, e[4 * c + 3] / s));
+            for (int j = 0; j < N; ++j)
+                if (j < cols) tile[lane * pitch + j] = e[j] / s;
+            wave_sync();
+            copy_out(a.y);
         }
     } else if constexpr (OP == kRowSum) {
-        a.sums[row] = lane_sum<POL>(x, cols);
+        const float sum = lane_sum<POL>(x, cols);
+        if (active) a.sums[row] = sum;
     } else if constexpr (OP == kRowMinMax) {
         float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
@@ -135,8 +156,10 @@ __global__ void __launch_bounds__(256) k_ordered_lane(const KArgs a) {
                 hi = fmax2(hi, x[j]);
             }
         }
-        if (a.mins) a.mins[row] = lo;
-        if (a.maxs) a.maxs[row] = hi;
+        if (active) {
+            if (a.mins) a.mins[row] = lo;
+            if (a.maxs) a.maxs[row] = hi;
+        }
     } else if constexpr (OP == kRmsNorm) {
         float q[N];
 #pragma unroll
@@ -144,16 +167,14 @@ __global__ void __launch_bounds__(256) k_ordered_lane(const KArgs a) {
         const float ms = lane_sum<POL>(q, cols) / n;
         const float r = 1.0f / sqrtf(ms + a.eps);
 #pragma unroll
-        for (int c = 0; c < N4; ++c) {
-            if (c < nv) {
-                float4 t = make_float4(x[4 * c] * r, x[4 * c + 1] * r, x[4 * c + 2] * r, x[4 * c + 3] * r);
-                if (a.gamma) {
-                    const float4 g = chunk_ld<AL>(a.gamma, c, true);
-                    t = make_float4(t.x * g.x, t.y * g.y, t.z * g.z, t.w * g.w);
-                }
-                chunk_st<AL>(a.y + roff, c, t);
+        for (int j = 0; j < N; ++j) {
+            if (j < cols) {
+                const float t = x[j] * r;
+                tile[lane * pitch + j] = a.gamma ? t * a.gamma[j] : t;
             }
         }
+        wave_sync();
+        copy_out(a.y);
     } else {  // LayerNorm, fused residual LayerNorm
         const float mu = lane_sum<POL>(x, cols) / n;
         float q[N];
@@ -165,64 +186,54 @@ __global__ void __launch_bounds__(256) k_ordered_lane(const KArgs a) {
         const float var = lane_sum<POL>(q, cols) / n;
         const float r = 1.0f / sqrtf(var + a.eps);
 #pragma unroll
-        for (int c = 0; c < N4; ++c) {
-            if (c < nv) {
-                float4 t = make_float4((x[4 * c] - mu) * r, (x[4 * c + 1] - mu) * r, (x[4 * c + 2] - mu) * r,
-                                       (x[4 * c + 3] - mu) * r);
-                if (a.gamma) {
-                    const float4 g = chunk_ld<AL>(a.gamma, c, true);
-                    t = make_float4(t.x * g.x, t.y * g.y, t.z * g.z, t.w * g.w);
-                }
-                if (a.beta) {
-                    const float4 b = chunk_ld<AL>(a.beta, c, true);
-                    t = make_float4(t.x + b.x, t.y + b.y, t.z + b.z, t.w + b.w);
-                }
-                chunk_st<AL>(a.y + roff, c, t);
+        for (int j = 0; j < N; ++j) {
+            if (j < cols) {
+                float t = (x[j] - mu) * r;
+                if (a.gamma) t = t * a.gamma[j];
+                if (a.beta) t = t + a.beta[j];
+                tile[lane * pitch + j] = t;
             }
         }
+        wave_sync();
+        copy_out(a.y);
     }
 }
 
-template <int OP, int POL, bool AL>
+template <int OP, int POL>
 hipError_t launch_lane_n4(const KArgs& a, const lr_plan& p, hipStream_t s) {
     const dim3 grid((unsigned)p.blocks), block(p.threads_per_block);
     switch (p.chunks_per_lane) {
-        case 1: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 1, AL>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 2, AL>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 4, AL>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 8, AL>), grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 16, AL>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 2>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 4>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 8>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 16>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <int POL, bool AL>
-hipError_t launch_lane_op(int op, const KArgs& a, const lr_plan& p, hipStream_t s) {
+template <int POL>
+hipError_t launch_lane_pol(int op, const KArgs& a, const lr_plan& p, hipStream_t s) {
     switch (op) {
-        case kSoftmax: return launch_lane_n4<kSoftmax, POL, AL>(a, p, s);
-        case kRmsNorm: return launch_lane_n4<kRmsNorm, POL, AL>(a, p, s);
-        case kLayerNorm: return launch_lane_n4<kLayerNorm, POL, AL>(a, p, s);
-        case kCrossEntropy: return launch_lane_n4<kCrossEntropy, POL, AL>(a, p, s);
-        case kAddLayerNorm: return launch_lane_n4<kAddLayerNorm, POL, AL>(a, p, s);
-        case kRowSum: return launch_lane_n4<kRowSum, POL, AL>(a, p, s);
-        case kRowMinMax: return launch_lane_n4<kRowMinMax, POL, AL>(a, p, s);
+        case kSoftmax: return launch_lane_n4<kSoftmax, POL>(a, p, s);
+        case kRmsNorm: return launch_lane_n4<kRmsNorm, POL>(a, p, s);
+        case kLayerNorm: return launch_lane_n4<kLayerNorm, POL>(a, p, s);
+        case kCrossEntropy: return launch_lane_n4<kCrossEntropy, POL>(a, p, s);
+        case kAddLayerNorm: return launch_lane_n4<kAddLayerNorm, POL>(a, p, s);
+        case kRowSum: return launch_lane_n4<kRowSum, POL>(a, p, s);
+        case kRowMinMax: return launch_lane_n4<kRowMinMax, POL>(a, p, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int POL>
-hipError_t launch_lane_pol(int op, const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s) {
-    return aligned ? launch_lane_op<POL, true>(op, a, p, s) : launch_lane_op<POL, false>(op, a, p, s);
-}
-
 }  // namespace
 
-hipError_t launch_ordered_lane(int op, int policy, const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s) {
+hipError_t launch_ordered_lane(int op, int policy, const KArgs& a, const lr_plan& p, hipStream_t s) {
     switch (policy) {
-        case kPolFoldLeft: return launch_lane_pol<kPolFoldLeft>(op, a, p, aligned, s);
-        case kPolTree: return launch_lane_pol<kPolTree>(op, a, p, aligned, s);
-        case kPolFoldRight: return launch_lane_pol<kPolFoldRight>(op, a, p, aligned, s);
+        case kPolFoldLeft: return launch_lane_pol<kPolFoldLeft>(op, a, p, s);
+        case kPolTree: return launch_lane_pol<kPolTree>(op, a, p, s);
+        case kPolFoldRight: return launch_lane_pol<kPolFoldRight>(op, a, p, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -153,7 +153,7 @@ lr_status validate_call(const Call& c) {
 
 hipError_t launch_piece(int op, int policy, const KArgs& a, const lr_plan& plan, bool aligned, hipStream_t stream) {
     if (plan.family == LR_FAMILY_ORDERED) {
-        return plan.lanes_per_row == 1 ? launch_ordered_lane(op, policy, a, plan, aligned, stream)
+        return plan.lanes_per_row == 1 ? launch_ordered_lane(op, policy, a, plan, stream)
                                        : launch_ordered(op, policy, a, plan, stream);
     }
     if (plan.family == LR_FAMILY_TREE) {

@@ -82,9 +82,9 @@ hipError_t launch_add_layernorm(const KArgs& a, const lr_plan& p, bool aligned, 
 hipError_t launch_row_sum(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_row_minmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_ordered(int op, int policy, const KArgs& a, const lr_plan& p, hipStream_t s);
-// The ordered policies with one lane per row (lanes_per_row = 1, narrow
-// aligned rows); `aligned`: every row pointer is 16-byte aligned.
-hipError_t launch_ordered_lane(int op, int policy, const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+// The ordered policies with one lane per row (lanes_per_row = 1: narrow
+// rows, one wavefront of 64 rows per workgroup).
+hipError_t launch_ordered_lane(int op, int policy, const KArgs& a, const lr_plan& p, hipStream_t s);
 // TREE family (ordered_tree on the cache layout), one translation unit per op.
 hipError_t launch_tree_softmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_tree_cross_entropy(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);

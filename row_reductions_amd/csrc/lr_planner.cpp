@@ -111,7 +111,7 @@ static lr_plan make_plan(int family, int S, int Q, int nch, int64_t rows, int64_
     p.splits = family == LR_FAMILY_SPLIT ? splits : 0;
     p.blocks = family == LR_FAMILY_SPLIT ? rows * splits : (rows + Q - 1) / Q;
     p.reductions = reductions_of(op);
-    p.lds_bytes = family == LR_FAMILY_ORDERED ? (lanes == 1 ? 0 : Q * (kSlab + kTreeStack) * 4)
+    p.lds_bytes = family == LR_FAMILY_ORDERED ? (lanes == 1 ? kWave * (kVec * nch + 1) * 4 : Q * (kSlab + kTreeStack) * 4)
                   : family == LR_FAMILY_TREE  ? 2 * kMaxWaves * 4 + 2 * kMaxWaves * 128 * 4
                                               : 2 * kMaxWaves * 4;
     p.row_aligned = aligned ? 1 : 0;
@@ -150,15 +150,15 @@ lr_status validate_plan(const lr_device_facts* f, int op, int64_t rows, int64_t 
     const int S = p->waves_per_row, Q = p->rows_per_block, L = p->lanes_per_row;
     if (!family_allowed(policy, p->family)) return LR_ERR_UNREALIZABLE_PLAN;
     if (L == 1) {
-        // one lane per row: ORDERED, aligned rows of whole chunks held in a
-        // compiled register stripe, whole waves per workgroup (<= 256 lanes)
-        if (p->family != LR_FAMILY_ORDERED || S != 1 || Q < kWave || Q % kWave != 0 || Q > 256)
-            return LR_ERR_UNREALIZABLE_PLAN;
-        if (!aligned || p->threads_per_block != Q || p->vec != 1 || p->splits != 0) return LR_ERR_UNREALIZABLE_PLAN;
+        // one lane per row: ORDERED, one wavefront of 64 rows per workgroup
+        // (the kernel's LDS tile holds exactly that), rows held in a compiled
+        // register stripe of 4 * chunks_per_lane >= cols floats, any alignment
+        if (p->family != LR_FAMILY_ORDERED || S != 1 || Q != kWave) return LR_ERR_UNREALIZABLE_PLAN;
+        if (p->threads_per_block != Q || p->vec != 1 || p->splits != 0) return LR_ERR_UNREALIZABLE_PLAN;
         if (p->blocks != (rows + Q - 1) / Q || p->blocks > INT32_MAX) return LR_ERR_UNREALIZABLE_PLAN;
         bool compiled = false;
         for (int i = 0; i < kNumLaneChunks; ++i) compiled = compiled || kLaneChunks[i] == p->chunks_per_lane;
-        if (!compiled || p->chunks_per_lane < cols / kVec) return LR_ERR_UNREALIZABLE_PLAN;
+        if (!compiled || (int64_t)kVec * p->chunks_per_lane < cols) return LR_ERR_UNREALIZABLE_PLAN;
         return LR_OK;
     }
     if (narrow_lanes(L)) {
@@ -239,12 +239,10 @@ static int enumerate_all(const lr_device_facts* f, int op, int64_t rows, int64_t
             }
         }
         for (int Q = 1; Q <= kMaxWaves; ++Q) push(make_plan(LR_FAMILY_ORDERED, 1, Q, 0, rows, cols, op, aligned));
-        // one lane per row: narrow aligned rows, 1, 2 or 4 waves per workgroup
-        if (aligned) {
-            const int n4 = smallest_lane_instance(nv);
-            if (n4 != 0)
-                for (int w = 1; w <= 4; w *= 2)
-                    push(make_plan(LR_FAMILY_ORDERED, 1, w * kWave, n4, rows, cols, op, aligned, 0, 1));
+        // one lane per row: narrow rows, one wavefront per workgroup
+        {
+            const int n4 = smallest_lane_instance((cols + kVec - 1) / kVec);
+            if (n4 != 0) push(make_plan(LR_FAMILY_ORDERED, 1, kWave, n4, rows, cols, op, aligned, 0, 1));
         }
         return n;
     }
@@ -386,14 +384,12 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
             if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
         }
         // the folds (and the tree on misaligned rows): rows plentiful and at
-        // most 8 chunks wide take one lane per row, others one wave per row.
-        // At 16 chunks a lane's row spans two 128-byte lines and a wave's 64
-        // rows 16 KB, which the lane-per-row loads touch one line per lane per
-        // access: on MI355X RMSNorm 262144 x 64 took 218 us that way against
-        // 123 us one wave per row; at 32 columns cross-entropy took 28 us
-        // against 104 us, and softmax 1048576 x 16 101 us against 850 us.
-        if (S == 1 && aligned && nv <= 8) {
-            const int n4 = smallest_lane_instance(nv);
+        // most 64 floats wide take one lane per row (on MI355X: RMSNorm
+        // 262144 x 64 80 us against 124 us one wave per row, 262144 x 50 67
+        // against 123 us, cross-entropy 262144 x 32 21 against 104 us,
+        // softmax 1048576 x 16 43 against 850 us); wider rows one wave per row
+        if (S == 1 && cols <= kVec * kLaneChunks[kNumLaneChunks - 1]) {
+            const int n4 = smallest_lane_instance((cols + kVec - 1) / kVec);
             lr_plan p = make_plan(LR_FAMILY_ORDERED, 1, kWave, n4, rows, cols, op, aligned, 0, 1);
             if (n4 != 0 && validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
         }
@@ -500,8 +496,7 @@ extern "C" lr_status lr_coverage_check(const lr_plan* p, int64_t rows, int64_t c
             for (int tid = 0; tid < Q; ++tid) {
                 const int64_t row = b * Q + tid;
                 if (row >= rows) continue;
-                for (int k = 0; k < p->chunks_per_lane && k < cols / kVec; ++k)
-                    for (int j = 0; j < kVec; ++j) counts[row * cols + kVec * k + j] += 1;
+                for (int j = 0; j < kVec * p->chunks_per_lane && j < cols; ++j) counts[row * cols + j] += 1;
             }
         return LR_OK;
     }

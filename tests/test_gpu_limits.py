@@ -141,15 +141,16 @@ def tall():
 
 
 def whole_wave_plan(op, policy):
-    """the automatic plan, or for the unordered policy (whose automatic plan
-    packs several rows per wave) the whole-wave CACHE plan with 16 rows per
-    workgroup"""
+    """the automatic plan when it gives each row a whole wave, else (the
+    automatic plan packs several rows per wave, or one row per lane) the
+    whole-wave CACHE or ORDERED plan with 16 rows per workgroup"""
     plan = lr.lr_plan_query(op, TALL, 1, policy)
     if plan.lanes_per_row == 64:
         return plan
     facts = lr.lr_device_facts_query()
     return next(p for p in lr.lr_plan_enumerate(facts, op, TALL, 1, policy, 0)
-                if p.family == lr.LR_FAMILY_CACHE and p.lanes_per_row == 64 and p.rows_per_block == 16)
+                if p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_ORDERED) and p.lanes_per_row == 64
+                and p.rows_per_block == 16)
 
 
 @pytest.mark.parametrize("op,policy", [(o, "unordered_tree") for o in

@@ -228,7 +228,7 @@ def test_negative_zero_rows_under_ordered_policies(cols):
                 assert np.array_equal(got.view(np.uint32), rep.view(np.uint32)), (pol, cols, plan, got, rep)
 
 
-LANE_COLS = [4, 8, 20, 32, 48, 64]
+LANE_COLS = [3, 4, 8, 17, 20, 32, 48, 50, 63, 64]  # misaligned rows included
 
 
 def run_op(op, d, cols, policy, plan, rows=ROWS):
@@ -264,14 +264,14 @@ def run_op(op, d, cols, policy, plan, rows=ROWS):
 @pytest.mark.parametrize("cols", LANE_COLS)
 @pytest.mark.parametrize("op", OPS)
 def test_one_lane_per_row_ordered(op, cols):
-    """the ordered policies with one lane per row (narrow aligned rows): the
+    """the ordered policies with one lane per row (narrow rows, any alignment): the
     FP32 replays bit for bit (norms, sums), the widened bar (softmax,
     cross-entropy), exact min / max, and every output bit-identical to the
     one-wave-per-row plan's: the same order and the same functions"""
     d = inputs(op, cols, seed=200 + cols)
     facts = lr.lr_device_facts_query()
     for policy in ("ordered_fold", "fold_right", "ordered_tree"):
-        plans = lr.lr_plan_enumerate(facts, op, ROWS, cols, policy, 1)
+        plans = lr.lr_plan_enumerate(facts, op, ROWS, cols, policy, 1 if cols % 4 == 0 else 0)
         lanes = [p for p in plans if p.lanes_per_row == 1]
         wave = next(p for p in plans if p.family == lr.LR_FAMILY_ORDERED and p.lanes_per_row == 64)
         assert lanes, (op, cols, policy)

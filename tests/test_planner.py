@@ -57,8 +57,12 @@ def test_plans_respect_device_limits():
         for rows, cols in [(1, 1), (37, 1537), (768, 6144), (4096, 32000), (5, 100000)]:
             for policy in POLICIES:
                 for p in lr.lr_plan_enumerate(F, op, rows, cols, policy, 1 if cols % 4 == 0 else 0):
-                    if p.lanes_per_row < 64:  # sub-wave teams: CACHE, one wave's lanes shared by rows
-                        assert p.family == lr.LR_FAMILY_CACHE and p.waves_per_row == 1
+                    if p.lanes_per_row == 1:  # one lane per row: ORDERED, one wavefront of 64 rows
+                        assert p.family == lr.LR_FAMILY_ORDERED and p.waves_per_row == 1
+                        assert p.rows_per_block == p.threads_per_block == 64 and p.chunks_per_lane in (1, 2, 4, 8, 16)
+                        assert 4 * p.chunks_per_lane >= cols and p.lds_bytes == 64 * (4 * p.chunks_per_lane + 1) * 4
+                    elif p.lanes_per_row < 64:  # sub-wave teams: CACHE or TREE, one wave's lanes shared by rows
+                        assert p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_TREE) and p.waves_per_row == 1
                         assert p.lanes_per_row in (4, 8, 16, 32) and p.rows_per_block % (64 // p.lanes_per_row) == 0
                         assert p.threads_per_block == p.lanes_per_row * p.rows_per_block <= 1024
                         assert p.chunks_per_lane in (1, 2)
@@ -312,3 +316,20 @@ def test_dispatch_rows_keep_each_dispatch_within_2_31_work_items():
     p = lr.lr_plan_for_device(F, "softmax", tall, 1, "unordered_tree", 0)
     assert p.lanes_per_row == 4 and lr.lr_dispatch_rows(p, tall) == tall
     assert lr.lr_dispatch_rows(None, 5) == 0 and lr.lr_dispatch_rows(p, 0) == 0
+
+
+def test_prior_takes_one_lane_per_row_for_narrow_ordered_rows():
+    """many rows of at most 64 floats under an ordered policy: one lane per
+    row, at the smallest compiled width, aligned or not; wider rows and few
+    rows keep one wave per row"""
+    for cols, nch in ((1, 1), (16, 4), (32, 8), (50, 16), (64, 16)):
+        for aligned in (0, 1):
+            if aligned and cols % 4:
+                continue
+            for policy in ("ordered_fold", "ordered_tree", "fold_right"):
+                p = lr.lr_plan_for_device(F, "rmsnorm", 262144, cols, policy, aligned)
+                if policy == "ordered_tree" and aligned and cols >= 4:
+                    continue  # narrow TREE teams take aligned rows under the tree
+                assert p.lanes_per_row == 1 and p.chunks_per_lane == nch, (cols, aligned, policy, p)
+    assert lr.lr_plan_for_device(F, "rmsnorm", 262144, 65, "ordered_fold", 0).lanes_per_row == 64
+    assert lr.lr_plan_for_device(F, "rmsnorm", 8, 64, "ordered_fold", 1).lanes_per_row == 64
