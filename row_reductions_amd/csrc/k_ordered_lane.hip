@@ -63,15 +63,23 @@ __device__ __forceinline__ void wave_sync() {
 // f / cols, column f % cols); the tile's row pitch is odd, so that the 64
 // lanes reading one element of their own rows hit distinct banks.  Any row
 // alignment works, and the rows past the tensor's end are read as zeros and
-// never written (the buffer resources cover the existing rows only).
+// never written (the buffer resources cover the existing rows only).  The
+// copies and the element loops have no branches: a load past its resource
+// returns 0, a store past it is dropped, and an LDS write for a slot past
+// the row goes to a spare slot (the copies) or the row's pad column.  So every global load of a copy,
+// and of gamma / beta, is in flight before the first is used; loads left
+// inside `i < cols` branches were each waited for before the next one went
+// out, one memory round trip per element.
 template <int OP, int POL, int N4>
 __global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
     constexpr int N = 4 * N4;       // cols <= N
-    constexpr int PMAX = N + 1;     // odd pitch >= cols
-    __shared__ float tile[kWave * PMAX];
+    constexpr int PMAX = N + 1;     // largest pitch (cols <= N, N even)
+    constexpr int SPARE = kWave * PMAX;  // one spare slot per lane past the rows
+    __shared__ float tile[SPARE + kWave];
     const int lane = (int)threadIdx.x;
     const int cols = a.cols;
-    const int pitch = cols | 1;
+    // odd row pitch with at least one pad column (column `cols`)
+    const int pitch = (cols + 1) | 1;
     const int64_t r0 = (int64_t)blockIdx.x * kWave;  // the wave's first row
     const int64_t left = a.rows - r0;
     const int nr = left < kWave ? (int)left : kWave;  // its rows that exist (>= 1)
@@ -81,45 +89,88 @@ __global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
     const int64_t row = r0 + lane;
     const bool active = lane < nr;
 
-    // flat element f -> (tile row, column), with the quotient from the FP32
-    // reciprocal corrected to the exact one (f < 64 * cols <= 2^12)
-    auto place = [&](int f) {
-        int r = (int)((float)f * a.inv_cols);
-        if (r * cols > f) --r;
-        if ((r + 1) * cols <= f) ++r;
-        return r * pitch + (f - r * cols);
+    // Tile slots of this lane's flat elements f = lane + 64 i, i = 0, 1, ...:
+    // row f / cols, column f % cols, stepped 64 elements at a time (q rows and
+    // rem columns further on, one more row when the column passes cols) with
+    // full-rate adds only.  Past the wave's 64 rows (i >= cols) the slot is at
+    // least SPARE and clamps into the spare slots, which nothing reads back.
+    const int q = kWave / cols, rem = kWave - q * cols;
+    const int step = q * pitch + rem, wrap = pitch - cols;
+    struct Walk {
+        unsigned c, idx;
     };
-    auto copy_in = [&](const float* src, const float* add) {
-        const BufRes rs = make_res(src + off0, nflat * 4);
-        const BufRes ra = make_res(add ? add + off0 : nullptr, add ? nflat * 4 : 0);
+    auto walk0 = [&]() {
+        const int r = lane / cols;
+        return Walk{(unsigned)(lane - r * cols), (unsigned)(r * pitch + (lane - r * cols))};
+    };
+    auto next = [&](Walk& w) {
+        const unsigned c = w.c + rem;
+        const unsigned t = c - (unsigned)cols;    // wraps around (huge) when c < cols
+        w.c = min(c, t);
+        w.idx += (unsigned)step + (t < c ? (unsigned)wrap : 0u);
+    };
+    auto slot = [&](const Walk& w) { return (int)min(w.idx, (unsigned)(SPARE + lane)); };
+    // gamma, beta (read only where present): entry j alike in every lane;
+    // past cols, or when absent, the resources read 0
+    constexpr int NP = OP == kRmsNorm ? 1 : (OP == kLayerNorm || OP == kAddLayerNorm ? 2 : 0);
+    float g[NP >= 1 ? N : 1], b[NP == 2 ? N : 1];
+    if constexpr (NP >= 1) {
+        const BufRes rg = make_res(a.gamma, a.gamma ? cols * 4 : 0);
+#pragma unroll
+        for (int j = 0; j < N; ++j) g[j] = res_ld1(rg, j * 4);
+    }
+    if constexpr (NP == 2) {
+        const BufRes rb = make_res(a.beta, a.beta ? cols * 4 : 0);
+#pragma unroll
+        for (int j = 0; j < N; ++j) b[j] = res_ld1(rb, j * 4);
+    }
+    // cross-entropy: the row's label, read with the parameters, ahead of the rows
+    int64_t lab = -1;
+    if constexpr (OP == kCrossEntropy) {
+        if (active) lab = a.labels[row];
+    }
+    // the rows (x + residual for the fused residual LayerNorm, in FP32)
+    {
+        const BufRes rs = make_res(a.x + off0, nflat * 4);
+        float v[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = res_ld1(rs, (lane + kWave * i) * 4);
+        if constexpr (OP == kAddLayerNorm) {
+            const BufRes ra = make_res(a.residual + off0, nflat * 4);
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = v[i] + res_ld1(ra, (lane + kWave * i) * 4);
+        }
+        Walk w = walk0();
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int f = lane + kWave * i;
-            if (i < cols) {
-                float v = res_ld1(rs, f * 4);
-                if (add) v = v + res_ld1(ra, f * 4);
-                tile[place(f)] = v;
-            }
+            tile[slot(w)] = v[i];
+            next(w);
         }
-    };
+    }
+    // the tile to `dst`: every read first (slots past the rows read entry 0),
+    // then the stores (those past the block are dropped)
     auto copy_out = [&](float* dst) {
         const BufRes rd = make_res(dst + off0, nflat * 4);
+        float o[N];
+        Walk w = walk0();
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int f = lane + kWave * i;
-            if (i < cols) res_st1(rd, f * 4, tile[place(f)]);
+            o[i] = tile[slot(w)];
+            next(w);
         }
+#pragma unroll
+        for (int i = 0; i < N; ++i) res_st1(rd, (lane + kWave * i) * 4, o[i]);
     };
-
-    // the rows (x + residual for the fused residual LayerNorm, in FP32)
-    copy_in(a.x, OP == kAddLayerNorm ? a.residual : nullptr);
     wave_sync();
     if constexpr (OP == kAddLayerNorm) {
         if (a.sum_out != nullptr) copy_out(a.sum_out);
     }
     float x[N];
 #pragma unroll
-    for (int j = 0; j < N; ++j) x[j] = j < cols ? tile[lane * pitch + j] : 0.0f;
+    for (int j = 0; j < N; ++j) {
+        const float t = tile[lane * pitch + j];  // inside the tile for every j < N
+        x[j] = j < cols ? t : 0.0f;
+    }
     wave_sync();  // every lane has its row before any lane writes the tile
 
     if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
@@ -133,14 +184,13 @@ __global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
         const float s = lane_sum<POL>(e, cols);
         if constexpr (OP == kCrossEntropy) {
             if (active) {
-                const int64_t lab = a.labels[row];
                 const float sel = (lab >= 0 && lab < (int64_t)cols) ? a.x[row * (int64_t)cols + lab] : 0.0f;
                 a.losses[row] = logf(s) + (m - sel);
             }
         } else {
 #pragma unroll
             for (int j = 0; j < N; ++j)
-                if (j < cols) tile[lane * pitch + j] = e[j] / s;
+                tile[lane * pitch + min(j, cols)] = e[j] / s;
             wave_sync();
             copy_out(a.y);
         }
@@ -168,10 +218,8 @@ __global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
         const float r = 1.0f / sqrtf(ms + a.eps);
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            if (j < cols) {
-                const float t = x[j] * r;
-                tile[lane * pitch + j] = a.gamma ? t * a.gamma[j] : t;
-            }
+            const float t = x[j] * r;
+            tile[lane * pitch + min(j, cols)] = a.gamma ? t * g[j] : t;
         }
         wave_sync();
         copy_out(a.y);
@@ -187,12 +235,10 @@ __global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
         const float r = 1.0f / sqrtf(var + a.eps);
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            if (j < cols) {
-                float t = (x[j] - mu) * r;
-                if (a.gamma) t = t * a.gamma[j];
-                if (a.beta) t = t + a.beta[j];
-                tile[lane * pitch + j] = t;
-            }
+            float t = (x[j] - mu) * r;
+            if (a.gamma) t = t * g[j];
+            if (a.beta) t = t + b[j];
+            tile[lane * pitch + min(j, cols)] = t;
         }
         wave_sync();
         copy_out(a.y);

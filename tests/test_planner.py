@@ -60,7 +60,7 @@ def test_plans_respect_device_limits():
                     if p.lanes_per_row == 1:  # one lane per row: ORDERED, one wavefront of 64 rows
                         assert p.family == lr.LR_FAMILY_ORDERED and p.waves_per_row == 1
                         assert p.rows_per_block == p.threads_per_block == 64 and p.chunks_per_lane in (1, 2, 4, 8, 16)
-                        assert 4 * p.chunks_per_lane >= cols and p.lds_bytes == 64 * (4 * p.chunks_per_lane + 1) * 4
+                        assert 4 * p.chunks_per_lane >= cols and p.lds_bytes == 64 * (4 * p.chunks_per_lane + 2) * 4
                     elif p.lanes_per_row < 64:  # sub-wave teams: CACHE or TREE, one wave's lanes shared by rows
                         assert p.family in (lr.LR_FAMILY_CACHE, lr.LR_FAMILY_TREE) and p.waves_per_row == 1
                         assert p.lanes_per_row in (4, 8, 16, 32) and p.rows_per_block % (64 // p.lanes_per_row) == 0
