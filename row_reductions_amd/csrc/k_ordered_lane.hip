@@ -70,14 +70,20 @@ __device__ __forceinline__ void wave_sync() {
 // and of gamma / beta, is in flight before the first is used; loads left
 // inside `i < cols` branches were each waited for before the next one went
 // out, one memory round trip per element.
-template <int OP, int POL, int N4>
-__global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
+// FULL: cols == N, a compile-time constant, so that no element loop keeps
+// a `j < cols` test.
+template <int N>
+constexpr int lane_tile_floats() {
+    return kWave * (N + 1) + kWave;  // 64 rows of pitch <= N + 1, the spare slots
+}
+
+template <int OP, int POL, int N4, bool FULL>
+__device__ __forceinline__ void lane_body(const KArgs& a, float* tile) {
     constexpr int N = 4 * N4;       // cols <= N
     constexpr int PMAX = N + 1;     // largest pitch (cols <= N, N even)
     constexpr int SPARE = kWave * PMAX;  // one spare slot per lane past the rows
-    __shared__ float tile[SPARE + kWave];
     const int lane = (int)threadIdx.x;
-    const int cols = a.cols;
+    const int cols = FULL ? N : a.cols;
     // odd row pitch with at least one pad column (column `cols`)
     const int pitch = (cols + 1) | 1;
     const int64_t r0 = (int64_t)blockIdx.x * kWave;  // the wave's first row
@@ -242,6 +248,16 @@ __global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
         }
         wave_sync();
         copy_out(a.y);
+    }
+}
+
+template <int OP, int POL, int N4>
+__global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
+    __shared__ float tile[lane_tile_floats<4 * N4>()];
+    if (a.cols == 4 * N4) {
+        lane_body<OP, POL, N4, true>(a, tile);
+    } else {
+        lane_body<OP, POL, N4, false>(a, tile);
     }
 }
 

@@ -385,9 +385,9 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
         }
         // the folds (and the tree on misaligned rows): rows plentiful and at
         // most 64 floats wide take one lane per row (on MI355X: RMSNorm
-        // 262144 x 64 27 us against 124 us one wave per row, 262144 x 50 23
-        // against 124 us, cross-entropy 262144 x 32 13 against 104 us,
-        // softmax 1048576 x 16 34 against 848 us); wider rows one wave per row
+        // 262144 x 64 26 us against 124 us one wave per row, 262144 x 50 23
+        // against 123 us, cross-entropy 262144 x 32 9 against 104 us,
+        // softmax 1048576 x 16 25 against 848 us); wider rows one wave per row
         if (S == 1 && cols <= kVec * kLaneChunks[kNumLaneChunks - 1]) {
             const int n4 = smallest_lane_instance((cols + kVec - 1) / kVec);
             lr_plan p = make_plan(LR_FAMILY_ORDERED, 1, kWave, n4, rows, cols, op, aligned, 0, 1);
