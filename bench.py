@@ -323,12 +323,16 @@ def main():
         nx = [torch.randn(262144, 64, device=dev) for _ in range(4)]
         ny = [torch.empty_like(t) for t in nx]
         ng, nb = torch.rand(64, device=dev) + 0.5, torch.randn(64, device=dev) * 0.1
-        for name, op, fn in (
-            ("softmax_262144x64_cold", "softmax",
+        for name, op, pol, fn in (
+            ("softmax_262144x64_cold", "softmax", 0,
              lambda i: lr.lib.lr_softmax_f32(nx[i % 4].data_ptr(), ny[i % 4].data_ptr(), 262144, 64, 0, sh)),
-            ("layernorm_262144x64_cold", "layernorm",
+            ("layernorm_262144x64_cold", "layernorm", 0,
              lambda i: lr.lib.lr_layernorm_f32(nx[i % 4].data_ptr(), ng.data_ptr(), nb.data_ptr(),
-                                               ny[i % 4].data_ptr(), 262144, 64, 1e-5, 0, sh))):
+                                               ny[i % 4].data_ptr(), 262144, 64, 1e-5, 0, sh)),
+            # the ordered fold with one lane per row
+            ("rmsnorm_262144x64_ordered_fold_cold", "rmsnorm", 1,
+             lambda i: lr.lib.lr_rmsnorm_f32(nx[i % 4].data_ptr(), ng.data_ptr(), ny[i % 4].data_ptr(), 262144, 64,
+                                             1e-6, 1, sh))):
             for i in range(8):
                 lr.check(fn(i), name)
             torch.cuda.synchronize()
@@ -340,7 +344,7 @@ def main():
             torch.cuda.synchronize()
             us = a.elapsed_time(z) * 1e3 / n
             nbytes = op_bytes(262144, 64)
-            p = lr.lr_plan_query(op, 262144, 64)
+            p = lr.lr_plan_query(op, 262144, 64, pol)
             extra[name] = {"us_per_op": round(us, 3), "gbps": round(nbytes / us / 1e3, 1),
                            "pct_of_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": nbytes,
                            "plan": {k: v for k, v in p.as_dict().items() if k in (
