@@ -130,7 +130,8 @@ __device__ __forceinline__ void lane_body(const KArgs& a, float* tile) {
 #pragma unroll
         for (int j = 0; j < N; ++j) b[j] = res_ld1(rb, j * 4);
     }
-    // cross-entropy: the row's label, read with the parameters, ahead of the rows
+    // cross-entropy: the row's label, read with the parameters, ahead of the
+    // rows (-1 for the lanes past the tensor's last row)
     int64_t lab = -1;
     if constexpr (OP == kCrossEntropy) {
         if (active) lab = a.labels[row];
@@ -177,6 +178,14 @@ __device__ __forceinline__ void lane_body(const KArgs& a, float* tile) {
         const float t = tile[lane * pitch + j];  // inside the tile for every j < N
         x[j] = j < cols ? t : 0.0f;
     }
+    // cross-entropy: the labelled logit, from the lane's row in the tile (0
+    // for a label outside [0, cols))
+    float sel = 0.0f;
+    if constexpr (OP == kCrossEntropy) {
+        const bool in = lab >= 0 && lab < (int64_t)cols;
+        const float t = tile[lane * pitch + (in ? (int)lab : 0)];
+        sel = in ? t : 0.0f;
+    }
     wave_sync();  // every lane has its row before any lane writes the tile
 
     if constexpr (OP == kSoftmax || OP == kCrossEntropy) {
@@ -190,7 +199,6 @@ __device__ __forceinline__ void lane_body(const KArgs& a, float* tile) {
         const float s = lane_sum<POL>(e, cols);
         if constexpr (OP == kCrossEntropy) {
             if (active) {
-                const float sel = (lab >= 0 && lab < (int64_t)cols) ? a.x[row * (int64_t)cols + lab] : 0.0f;
                 a.losses[row] = logf(s) + (m - sel);
             }
         } else {

@@ -138,6 +138,7 @@ __device__ __forceinline__ float team_reduce(float v, float* slots, int S, const
 #endif
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Row-stream load.
 __device__ __forceinline__ float4 ld4(const float4* p) {
