@@ -15,7 +15,7 @@ import torch
 import oracle
 import row_reductions_amd as lr
 import synth
-from gpu_util import ATOL, DEV, RTOL, assert_parity, guards_intact, placed
+from gpu_util import ATOL, DEV, RTOL, assert_parity, bits_equal, guards_intact, placed
 
 pytestmark = pytest.mark.gpu
 
@@ -297,3 +297,66 @@ def test_one_lane_per_row_ordered(op, cols):
                 else:
                     rep = np.array([oracle.ordered_sum_f32(r, policy) for r in x], dtype=np.float32)
                 assert np.array_equal(got1.view(np.uint32), rep.view(np.uint32)), what
+
+
+EDGE_COLS = [16, 50]  # the constant-width body (16 = 4 * 4 floats) and the general one
+
+
+@pytest.mark.parametrize("cols", EDGE_COLS)
+def test_one_lane_per_row_edges(cols):
+    """one lane per row under ordered_fold, with input and output rows at
+    4-byte offsets from the 16-byte grid, in place, gamma / beta absent, and
+    the fused residual LayerNorm's combined output: every output between
+    intact guard regions; the norms equal the FP32 replays of the policy
+    ("TIRx Metal reduction lowering", section 1, the reduction policies) and
+    softmax the one-wave-per-row plan, bit for bit"""
+    facts = lr.lr_device_facts_query()
+    d = inputs("add_layernorm", cols, seed=300 + cols)
+    x, res = d["x"], d["residual"]
+    policy = "ordered_fold"
+
+    def plan_of(op, lanes):
+        return next(p for p in lr.lr_plan_enumerate(facts, op, ROWS, cols, policy, 0)
+                    if p.lanes_per_row == lanes and p.family == lr.LR_FAMILY_ORDERED)
+
+    wave_softmax, _ = run_op("softmax", d, cols, policy, plan_of("softmax", 64))
+    for xo, yo, in_place, params in ((1, 3, False, True), (2, 2, True, False), (3, 0, False, False)):
+        what = f"{ROWS}x{cols} xo={xo} yo={yo} in_place={in_place} gamma/beta={params}"
+        print(f"\n[gpu] lane edges {what}", flush=True)
+        g = torch.from_numpy(d["gamma"]).to(DEV) if params else None
+        b = torch.from_numpy(d["beta"]).to(DEV) if params else None
+        gam, bet = (d["gamma"], d["beta"]) if params else (None, None)
+
+        def out_for(xv, xf):
+            return (xv, xf) if in_place else placed(np.zeros_like(x), yo)
+
+        xv, xf = placed(x, xo)
+        yv, yf = out_for(xv, xf)
+        st = lr.lr_rmsnorm_f32(xv, g, yv, ROWS, cols, EPS["rmsnorm"], policy, plan=plan_of("rmsnorm", 1))
+        torch.cuda.synchronize()
+        assert st == lr.LR_OK, lr.lr_status_string(st)
+        assert guards_intact(yv, yf), "rmsnorm " + what
+        bits_equal(yv.cpu().numpy(), oracle.rmsnorm_ordered_f32(x, gam, EPS["rmsnorm"], policy), "rmsnorm " + what)
+
+        xv, xf = placed(x, xo)
+        rv, _ = placed(res, xo)
+        yv, yf = out_for(xv, xf)
+        sv, sf = placed(np.zeros_like(x), yo)
+        st = lr.lr_add_layernorm_f32(xv, rv, g, b, yv, sv, ROWS, cols, EPS["add_layernorm"], policy,
+                                     plan=plan_of("add_layernorm", 1))
+        torch.cuda.synchronize()
+        assert st == lr.LR_OK, lr.lr_status_string(st)
+        assert guards_intact(yv, yf) and guards_intact(sv, sf), "add_layernorm " + what
+        _, comb = oracle.add_layernorm(x, res, None, None, EPS["add_layernorm"], with_sum=True)
+        comb = comb.astype(np.float32)
+        bits_equal(sv.cpu().numpy(), comb, "add_layernorm sum " + what)
+        bits_equal(yv.cpu().numpy(), oracle.layernorm_ordered_f32(comb, gam, bet, EPS["add_layernorm"], policy),
+                   "add_layernorm " + what)
+
+        xv, xf = placed(x, xo)
+        yv, yf = out_for(xv, xf)
+        st = lr.lr_softmax_f32(xv, yv, ROWS, cols, policy, plan=plan_of("softmax", 1))
+        torch.cuda.synchronize()
+        assert st == lr.LR_OK, lr.lr_status_string(st)
+        assert guards_intact(yv, yf), "softmax " + what
+        bits_equal(yv.cpu().numpy(), wave_softmax, "softmax vs the wave plan " + what)
