@@ -114,10 +114,14 @@ typedef enum lr_op {
  * ORDERED: the ordered policies for any row: one wavefront per row, the row
  *          staged through LDS in 256-element slabs, folded in order
  *          (LR_ORDERED_FOLD, LR_FOLD_RIGHT) or summed as the pairwise tree
- *          (LR_ORDERED_TREE).
+ *          (LR_ORDERED_TREE).  Rows of at most 64 floats may instead take
+ *          one lane per row (lanes_per_row = 1): 64 rows per wavefront,
+ *          staged through an LDS tile, each lane's order its own chain.
  * TREE:    LR_ORDERED_TREE on the CACHE layout, for rows whose start is
  *          16-byte aligned and cols <= 32768: each wave's 256-element slab
- *          is one wave tree, and the slab sums one more.
+ *          is one wave tree, and the slab sums one more.  Narrow aligned
+ *          rows may take sub-wave teams (lanes_per_row = 4 .. 32, one
+ *          chunk per lane).
  * SPLIT:   LR_UNORDERED_TREE for rows too few to fill the device: each row
  *          is cut into `splits` segments of whole 16-byte chunks, one
  *          workgroup per segment.  A first kernel writes every segment's
@@ -151,7 +155,9 @@ typedef struct lr_plan {
                                   SPLIT: chunks per lane of one segment
                                   (1,2,3,4,6 or 8);
                                   STREAM: chunks loaded per lane per loop trip;
-                                  ORDERED: 0 */
+                                  ORDERED: 0, or with one lane per row the
+                                  instance width N4 (1,2,4,8 or 16; the row
+                                  fits 4 * N4 floats) */
     int32_t threads_per_block; /* 64 * S * Q, or lanes_per_row * Q */
     int64_t blocks;            /* ceil(rows / Q); SPLIT: rows * splits */
     int32_t lds_bytes;         /* static LDS the kernel uses */
@@ -161,10 +167,11 @@ typedef struct lr_plan {
                                   0 for every other family */
     int32_t lanes_per_row;     /* lanes serving one row: 64 * S (0 reads as
                                   64 * S, so a plan filled in field by field
-                                  without it keeps whole waves), or 4, 8, 16
-                                  or 32 for a CACHE plan of sub-wave teams
-                                  (S = 1, chunks_per_lane 1 or 2); the
-                                  planner always fills it in */
+                                  without it keeps whole waves); 4, 8, 16
+                                  or 32 for sub-wave teams (S = 1; CACHE
+                                  with chunks_per_lane 1 or 2, TREE with 1);
+                                  1 for ORDERED with one lane per row (S = 1,
+                                  Q = 64); the planner always fills it in */
 } lr_plan;
 
 /* What the planner needs to know about a device. */
