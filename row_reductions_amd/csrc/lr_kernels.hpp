@@ -233,6 +233,27 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
         lab = (int64_t)(((uint64_t)(uint32_t)w[1] << 32) | (uint32_t)w[0]);
     }
 
+    // narrow teams: gamma / beta (one or two chunks per lane, the same for
+    // every row) are read before the rows, so that the store loop does not
+    // wait for them after the reductions.  Whole-wave teams read them chunk
+    // by chunk in the store loop (see above).
+    float4 gpre[NARROW && NP >= 1 ? NCH : 1], bpre[NARROW && NP == 2 ? NCH : 1];
+    if constexpr (NARROW && NP >= 1) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            gpre[c] = param_load<AL, PM>(rg, a.gamma != nullptr, chunk(c), h, cols, 1.0f);
+            if constexpr (NP == 2) bpre[c] = param_load<AL, PM>(rb, a.beta != nullptr, chunk(c), h, cols, 0.0f);
+        }
+    }
+    auto gamma_of = [&](int c, int k) {
+        if constexpr (NARROW && NP >= 1) return gpre[c];
+        return param_load<AL, PM>(rg, a.gamma != nullptr, k, h, cols, 1.0f);
+    };
+    auto beta_of = [&](int c, int k) {
+        if constexpr (NARROW && NP == 2) return bpre[c];
+        return param_load<AL, PM>(rb, a.beta != nullptr, k, h, cols, 0.0f);
+    };
+
     float4 v[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -248,6 +269,21 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
         } else {
             v[c] = (k < nv) ? raw : splat4(ID);
             if (!AL) mask_chunk(v[c], k, h, cols, ID);
+        }
+    }
+
+    if constexpr (NARROW && NP >= 1) {
+        // the parameters are used only in the store loop's `k < nv` branch;
+        // without this the compiler moves their loads down there
+        auto pin = [](float4& q) {
+            float x = q.x, y = q.y, z = q.z, w = q.w;
+            asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
+            q = make_float4(x, y, z, w);
+        };
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            pin(gpre[c]);
+            if constexpr (NP == 2) pin(bpre[c]);
         }
     }
 
@@ -325,7 +361,7 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
         for (int c = 0; c < NCH; ++c) {
             const int k = chunk(c);
             if (k < nv) {
-                const float4 g = param_load<AL, PM>(rg, a.gamma != nullptr, k, h, cols, 1.0f);
+                const float4 g = gamma_of(c, k);
                 const float4 o = make_float4(v[c].x * r * g.x, v[c].y * r * g.y,
                                              v[c].z * r * g.z, v[c].w * r * g.w);
                 store_chunk<AL>(yr, a.y_same_phase, k, h, cols, o);
@@ -364,8 +400,8 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
         for (int c = 0; c < NCH; ++c) {
             const int k = chunk(c);
             if (k < nv) {
-                const float4 g = param_load<AL, PM>(rg, a.gamma != nullptr, k, h, cols, 1.0f);
-                const float4 b = param_load<AL, PM>(rb, a.beta != nullptr, k, h, cols, 0.0f);
+                const float4 g = gamma_of(c, k);
+                const float4 b = beta_of(c, k);
                 const float4 o = make_float4(v[c].x * r * g.x + b.x, v[c].y * r * g.y + b.y,
                                              v[c].z * r * g.z + b.z, v[c].w * r * g.w + b.w);
                 store_chunk<AL>(yr, a.y_same_phase, k, h, cols, o);
