@@ -225,8 +225,8 @@ __global__ void __launch_bounds__(1024) k_split_apply(const KArgs a) {
     load_segment<OP, NCH, AL, LR_NT_LOADS ? kAuxNt : kAuxDefault>(a, c, t.w, W, v);
     // the parameters do not depend on the statistics: their loads are in
     // flight while the partials merge
-    const BufRes rg = make_res(a.gamma, NP >= 1 && a.gamma ? cols * 4 : 0);
-    const BufRes rb = make_res(a.beta, NP == 2 && a.beta ? cols * 4 : 0);
+    const ParamRes rg = param_res<AL>(a.gamma, cols, NP >= 1 && a.gamma);
+    const ParamRes rb = param_res<AL>(a.beta, cols, NP == 2 && a.beta);
     float4 gv[NP >= 1 ? NCH : 1], bv[NP == 2 ? NCH : 1];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {

@@ -81,8 +81,8 @@ __device__ __forceinline__ void tree_body(const KArgs& a, float (&red)[2][kMaxWa
         rr = make_res(RES ? a.residual + off0 : nullptr, RES ? nr * cols * 4 : 0);
         xo = active ? (int)((row - r0) * cols * 4) : 0;
     }
-    const BufRes rg = make_res(a.gamma, num_params<OP>() >= 1 && a.gamma ? cols * 4 : 0);
-    const BufRes rb = make_res(a.beta, num_params<OP>() == 2 && a.beta ? cols * 4 : 0);
+    const ParamRes rg = param_res<AL>(a.gamma, cols, num_params<OP>() >= 1 && a.gamma);
+    const ParamRes rb = param_res<AL>(a.beta, cols, num_params<OP>() == 2 && a.beta);
     auto chunk = [&](int c) { return chunk_index(t.w, W, c); };
 
     // the row (x + residual for the fused residual LayerNorm); zeros past it

@@ -1,0 +1,78 @@
+"""gamma and beta at every 4-byte offset from the 16-byte grid, against rows
+at every phase, on the GPU: one plan of each family that reads the
+parameters (whole-wave and sub-wave CACHE, STREAM, split rows through a
+workspace), each within |gpu - ref| <= 1e-6 + 1e-5 |ref| of the double
+oracle ("TIRx Metal reduction lowering", section 8, the affine step).
+Parameters off the grid make every call take the misaligned kernels, which
+read each parameter chunk as the two 16-byte blocks of the parameter's own
+grid that cover it."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import row_reductions_amd as lr
+import synth
+from gpu_util import DEV, assert_parity, guards_intact, placed
+
+pytestmark = pytest.mark.gpu
+
+OPS = ["rmsnorm", "layernorm", "add_layernorm"]
+EPS = {"rmsnorm": 1e-6, "layernorm": 1e-5, "add_layernorm": 1e-5}
+SHAPES = [(157, 50), (157, 64), (40, 1537), (8, 6147)]  # narrow rows, then whole waves
+OFFSETS = [(0, 1, 2), (1, 3, 0), (2, 2, 2), (3, 0, 1)]  # (x and y, gamma, beta) in floats
+
+
+def plans_for(op, rows, cols):
+    """the first legal plan of each family for unaligned calls, plus a
+    sub-wave CACHE plan where there is one"""
+    facts = lr.lr_device_facts_query()
+    out = {}
+    for p in lr.lr_plan_enumerate(facts, op, rows, cols, "unordered_tree", 0):
+        key = (p.family, p.lanes_per_row < 64 * p.waves_per_row)
+        out.setdefault(key, p)
+    return list(out.values())
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("op", OPS)
+def test_parameters_off_the_grid(op, rows, cols):
+    if op == "rmsnorm":
+        d = synth.rmsnorm_inputs(rows, cols, seed=11)
+    elif op == "layernorm":
+        d = synth.layernorm_inputs(rows, cols, seed=12, mean=3.0, std=2.0)
+    else:
+        d = synth.add_layernorm_inputs(rows, cols, seed=13, mean=3.0, std=2.0)
+    x, gam = d["x"], d["gamma"]
+    bet = d.get("beta")
+    if op == "rmsnorm":
+        ref = oracle.rmsnorm(x, gam, EPS[op])
+    elif op == "layernorm":
+        ref = oracle.layernorm(x, gam, bet, EPS[op])
+    else:
+        ref = oracle.add_layernorm(x, d["residual"], gam, bet, EPS[op])
+    plans = plans_for(op, rows, cols)
+    assert {p.family for p in plans} >= {lr.LR_FAMILY_CACHE, lr.LR_FAMILY_STREAM}
+    for xo, go, bo in OFFSETS:
+        for plan in [None] + plans:
+            what = f"{op} {rows}x{cols} x/y+{xo} gamma+{go} beta+{bo} plan={plan}"
+            print(f"\n[gpu] params {what}", flush=True)
+            xv, _ = placed(x, xo)
+            yv, yf = placed(np.zeros_like(x), xo)
+            gv, _ = placed(gam, go)
+            bv = placed(bet, bo)[0] if bet is not None else None
+            ws = None
+            if plan is not None and plan.family == lr.LR_FAMILY_SPLIT:
+                ws = torch.zeros(lr.lr_plan_workspace_bytes(plan, rows), dtype=torch.uint8, device=DEV)
+            if op == "rmsnorm":
+                st = lr.lr_rmsnorm_f32(xv, gv, yv, rows, cols, EPS[op], plan=plan, workspace=ws)
+            elif op == "layernorm":
+                st = lr.lr_layernorm_f32(xv, gv, bv, yv, rows, cols, EPS[op], plan=plan, workspace=ws)
+            else:
+                rv, _ = placed(d["residual"], xo)
+                st = lr.lr_add_layernorm_f32(xv, rv, gv, bv, yv, None, rows, cols, EPS[op], plan=plan,
+                                             workspace=ws)
+            torch.cuda.synchronize()
+            assert st == lr.LR_OK, (what, lr.lr_status_string(st))
+            assert guards_intact(yv, yf), what
+            assert_parity(yv.cpu().numpy(), ref, what)
