@@ -221,14 +221,18 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
     const int nv = active ? (AL ? cols / kVec : chunks_of(h, cols)) : 0;
     const ParamRes rg = param_res<AL>(a.gamma, cols, NP >= 1 && a.gamma);
     const ParamRes rb = param_res<AL>(a.beta, cols, NP == 2 && a.beta);
-    // fused residual: aligned rows read it on the x grid, misaligned rows one
-    // float at a time (its phase need not match x's)
+    // fused residual: read on the x grid where its rows sit at x's phases
+    // (below), else one float at a time
     constexpr bool RES = OP == kAddLayerNorm;
     const int64_t roff = (active ? row : 0) * (int64_t)cols;
     BufRes rx, rr;
     int xo = 0, ro = 0;  // byte offsets of this lane's row in rx and rr
+    const float* rx_base;  // rx covers rx_bytes from rx_base
+    int rx_bytes;
     if constexpr (!NARROW) {
-        rx = make_res(xr - h, nv * 16);
+        rx_base = xr - h;
+        rx_bytes = nv * 16;
+        rx = make_res(rx_base, rx_bytes);
         rr = make_res(RES ? a.residual + roff : nullptr, RES && active ? (AL ? nv * 16 : cols * 4) : 0);
     } else {
         const int64_t r0 = row_of(blockIdx.x, a.Q, wave_id() * (kWave / LW));  // the wave's first row
@@ -237,7 +241,9 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
         const int64_t off0 = (nr > 0 ? r0 : 0) * (int64_t)cols;
         const int h0 = AL ? 0 : phase_of(reinterpret_cast<uintptr_t>(a.x + off0));
         const int xbytes = (nr * cols + h0 + kVec - 1) / kVec * 16;
-        rx = make_res(a.x + off0 - h0, xbytes);
+        rx_base = a.x + off0 - h0;
+        rx_bytes = xbytes;
+        rx = make_res(rx_base, xbytes);
         xo = active ? (int)(((row - r0) * cols - h + h0) * 4) : 0;
         rr = make_res(RES ? a.residual + off0 : nullptr, RES ? (AL ? xbytes : nr * cols * 4) : 0);
         ro = active ? (int)((row - r0) * cols * 4) : 0;
@@ -285,20 +291,37 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
         return param_load<AL, PM>(rb, a.beta != nullptr, k, h, cols, 0.0f);
     };
 
+    constexpr int AUX = LR_NT_LOADS ? kAuxNt : kAuxDefault;
     float4 v[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) v[c] = res_ld4<AUX>(rx, xo + chunk(c) * 16);
+    if constexpr (RES) {
+        // the residual: on aligned rows, and on misaligned rows when its
+        // tensor starts at x's phase (so every residual row sits at its x
+        // row's phase), the same 16-byte reads as x; otherwise one float at a
+        // time.  The choice is uniform and outside the loops, so that every
+        // path issues all its loads before the first use.
+        float4 q[NCH];
+        if constexpr (AL) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) q[c] = res_ld4<AUX>(rr, ro + chunk(c) * 16);
+        } else if (phase_of(reinterpret_cast<uintptr_t>(a.residual)) == phase_of(reinterpret_cast<uintptr_t>(a.x))) {
+            const BufRes rm = make_res(a.residual + (rx_base - a.x), rx_bytes);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) q[c] = res_ld4<AUX>(rm, xo + chunk(c) * 16);
+        } else {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) q[c] = elem_chunk(rr, chunk(c), h, cols, ro);
+        }
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            v[c] = make_float4(v[c].x + q[c].x, v[c].y + q[c].y, v[c].z + q[c].z, v[c].w + q[c].w);
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int k = chunk(c);
-        float4 raw = res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rx, xo + k * 16);
-        if constexpr (RES) {
-            const float4 q = AL ? res_ld4<LR_NT_LOADS ? kAuxNt : kAuxDefault>(rr, ro + k * 16)
-                                : elem_chunk(rr, k, h, cols, ro);
-            raw = make_float4(raw.x + q.x, raw.y + q.y, raw.z + q.z, raw.w + q.w);
-        }
-        if constexpr (ID == 0.0f && AL && !NARROW) {
-            v[c] = raw;  // past the end: zeros, the add identity
-        } else {
-            v[c] = (k < nv) ? raw : splat4(ID);
+        if constexpr (!(ID == 0.0f && AL && !NARROW)) {  // else past the end: zeros, the add identity
+            v[c] = (k < nv) ? v[c] : splat4(ID);
             if (!AL) mask_chunk(v[c], k, h, cols, ID);
         }
     }
