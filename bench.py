@@ -391,10 +391,14 @@ def small_configs_graph(lr, synth, torch, dev) -> dict:
     ly = torch.empty_like(lx)
     cases.append(("layernorm_64x12289", lambda sh: lr.lr_layernorm_f32(lx, lg, lb, ly, 64, 12289, 1e-5, 0, sh),
                   2 * lx.numel() * 4))
-    # the same with a workspace: rows split across workgroups (two kernels)
-    lws = torch.empty(lr.lr_workspace_query("layernorm", 64, 12289), dtype=torch.uint8, device=dev)
+    # the same with rows split across workgroups through a workspace (two
+    # kernels; the fastest split plan, given explicitly: the planner keeps
+    # one launch here, which is faster)
+    sp = next(p for p in lr.lr_plan_enumerate(lr.lr_device_facts_query(), "layernorm", 64, 12289, "unordered_tree", 0)
+              if p.family == lr.LR_FAMILY_SPLIT and p.splits == 4 and p.waves_per_row == 8 and p.chunks_per_lane == 2)
+    lws = torch.empty(lr.lr_plan_workspace_bytes(sp, 64), dtype=torch.uint8, device=dev)
     cases.append(("layernorm_64x12289_split",
-                  lambda sh: lr.lr_layernorm_f32(lx, lg, lb, ly, 64, 12289, 1e-5, 0, sh, workspace=lws),
+                  lambda sh: lr.lr_layernorm_f32(lx, lg, lb, ly, 64, 12289, 1e-5, 0, sh, plan=sp, workspace=lws),
                   2 * lx.numel() * 4))
     for name, fn, nbytes in cases:
         side = torch.cuda.Stream()

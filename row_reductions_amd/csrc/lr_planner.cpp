@@ -309,16 +309,16 @@ static const TableEntry kTable[] = {
 // segments per row, G the smallest power of two with rows*G >= the CU count,
 // halved while a segment would hold fewer than 256 chunks (1024 floats: the
 // second launch has to pay for itself); S the fewest waves with a stripe of
-// at most 4 chunks per lane.  G < 2 means: do not split.  Only the LayerNorms
-// split: on MI355X at 64 x 12289 their one-launch kernels take 10-12 us (two
-// statistics passes, then the gamma and beta reads), which a second launch
-// beats (8-9.4 us); softmax, RMSNorm, cross-entropy and the row sum finish
-// in 4-7 us in one launch, faster than any split plan.
+// at most 4 chunks per lane.  G < 2 means: do not split.  Only the fused
+// residual LayerNorm splits (three tensor streams per row): on MI355X at
+// 64 x 12288 in a graph, 5.1 us split against 5.6 us in one launch.  The
+// other ops finish faster in one launch than any split plan (LayerNorm
+// 64 x 12288 3.9 us, 64 x 12289 5.6 us; the split plans 4.7 and 6.2 us).
 static lr_plan split_prior(const lr_device_facts* f, int op, int64_t rows, int64_t cols, bool aligned) {
     lr_plan none;
     std::memset(&none, 0, sizeof(none));
     const int64_t cus = f->compute_units;
-    if (op != LR_OP_LAYERNORM && op != LR_OP_ADD_LAYERNORM) return none;
+    if (op != LR_OP_ADD_LAYERNORM) return none;
     if (rows < 1 || 2 * rows > cus) return none;
     int G = 1;
     while (G < kMaxSplits && rows * G < cus) G *= 2;

@@ -3,9 +3,10 @@
  * an RMSNorm and a cross-entropy on small inputs, checks them against
  * properties that hold exactly or nearly (rows of the softmax sum to one; the
  * RMSNorm of a constant row c is gamma * sign(c) at eps = 0; the
- * cross-entropy of a uniform row is log(cols)), runs a LayerNorm whose rows
- * are split across workgroups through lr_run_f32 and a workspace, and checks
- * that an invalid call returns its status before touching the device.  Prints "abi_client
+ * cross-entropy of a uniform row is log(cols)), runs a fused residual
+ * LayerNorm whose rows are split across workgroups through lr_run_f32 and a
+ * workspace, and checks that an invalid call returns its status before
+ * touching the device.  Prints "abi_client
  * ok" and exits 0 on success. */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -101,50 +102,55 @@ int main(void) {
         }
     }
 
-    /* LayerNorm through lr_run_f32 with a workspace: 8 rows of 4096 are too
-     * few to fill the device, so the automatic plan splits each row over
-     * several workgroups.  Rows alternate +2, -2: every segment's mean is 0
-     * and its sum of squared deviations is exact, so y = +-1 (eps = 0). */
+    /* The fused residual LayerNorm through lr_run_f32 with a workspace: 8
+     * rows of 4096 are too few to fill the device, so the automatic plan
+     * splits each row over several workgroups.  x alternates +2, -2 and the
+     * residual is 0: every segment's mean is 0 and its sum of squared
+     * deviations is exact, so y = +-1 (eps = 0). */
     {
         enum { LR_ROWS = 8, LR_COLS = 4096 };
         const size_t m = (size_t)LR_ROWS * LR_COLS;
         float* hz = (float*)malloc(m * sizeof(float));
-        float *dz, *dw;
+        float *dz, *dr, *dw;
         uint64_t ws = 0;
         lr_plan plan;
         lr_device_facts facts;
         if (!hz) return 1;
         for (size_t i = 0; i < m; ++i) hz[i] = (i % 2) ? -2.0f : 2.0f;
         CHECK_LR(lr_device_facts_query(&facts));
-        CHECK_LR(lr_plan_for_device_ws(&facts, LR_OP_LAYERNORM, LR_ROWS, LR_COLS, LR_UNORDERED_TREE, 1, &plan));
+        CHECK_LR(lr_plan_for_device_ws(&facts, LR_OP_ADD_LAYERNORM, LR_ROWS, LR_COLS, LR_UNORDERED_TREE, 1, &plan));
         if (plan.family != LR_FAMILY_SPLIT || plan.splits < 2) {
             fprintf(stderr, "expected a split plan, got family %d\n", plan.family);
             return 1;
         }
-        CHECK_LR(lr_workspace_query(LR_OP_LAYERNORM, LR_ROWS, LR_COLS, LR_UNORDERED_TREE, &ws));
+        CHECK_LR(lr_workspace_query(LR_OP_ADD_LAYERNORM, LR_ROWS, LR_COLS, LR_UNORDERED_TREE, &ws));
         if (ws < lr_plan_workspace_bytes(&plan, LR_ROWS) || ws == 0) return 1;
         CHECK_HIP(hipMalloc((void**)&dz, m * sizeof(float)));
         CHECK_HIP(hipMalloc((void**)&dw, ws));
+        CHECK_HIP(hipMalloc((void**)&dr, m * sizeof(float)));
         CHECK_HIP(hipMemcpy(dz, hz, m * sizeof(float), hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemset(dr, 0, m * sizeof(float)));
         lr_tensors t = {0};
         t.x = dz;
+        t.residual = dr;
         t.y = dz; /* in place */
-        CHECK_LR(lr_run_f32(LR_OP_LAYERNORM, &t, LR_ROWS, LR_COLS, 0.0f, LR_UNORDERED_TREE, NULL, dw, ws, NULL));
+        CHECK_LR(lr_run_f32(LR_OP_ADD_LAYERNORM, &t, LR_ROWS, LR_COLS, 0.0f, LR_UNORDERED_TREE, NULL, dw, ws, NULL));
         CHECK_HIP(hipDeviceSynchronize());
         CHECK_HIP(hipMemcpy(hz, dz, m * sizeof(float), hipMemcpyDeviceToHost));
         for (size_t i = 0; i < m; ++i) {
             const float want = (i % 2) ? -1.0f : 1.0f;
             if (fabsf(hz[i] - want) > 1e-6f) {
-                fprintf(stderr, "split layernorm [%zu] = %.9g, want %.9g\n", i, hz[i], want);
+                fprintf(stderr, "split add_layernorm [%zu] = %.9g, want %.9g\n", i, hz[i], want);
                 return 1;
             }
         }
         /* a member the operation does not use is an error */
         t.sums = dy;
-        if (lr_run_f32(LR_OP_LAYERNORM, &t, LR_ROWS, LR_COLS, 0.0f, LR_UNORDERED_TREE, NULL, dw, ws, NULL) !=
+        if (lr_run_f32(LR_OP_ADD_LAYERNORM, &t, LR_ROWS, LR_COLS, 0.0f, LR_UNORDERED_TREE, NULL, dw, ws, NULL) !=
             LR_ERR_INVALID_ARGUMENT)
             return 1;
         CHECK_HIP(hipFree(dz));
+        CHECK_HIP(hipFree(dr));
         CHECK_HIP(hipFree(dw));
         free(hz);
     }

@@ -97,16 +97,18 @@ def split_plan(op, rows, cols, G=4, S=4):
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("cols", [12289, 12288])
 def test_split_at_the_layernorm_workload_shape(op, cols):
-    """the LayerNorms split automatically at 64 rows; every op splits under an
-    explicit plan, and a fixed plan gives the same bits twice"""
+    """the fused residual LayerNorm splits automatically at 64 x 12288; every
+    op splits under an explicit plan, and a fixed plan gives the same bits
+    twice"""
     rows = 64
     print(f"\n[gpu] split {op} {rows}x{cols}", flush=True)
     need = lr.lr_workspace_query(op, rows, cols)
     facts = lr.lr_device_facts_query()
     auto = lr.lr_plan_for_device_ws(facts, op, rows, cols, "unordered_tree", 1 if cols % 4 == 0 else 0)
-    plan = auto if op in ("layernorm", "add_layernorm") else split_plan(op, rows, cols)
+    auto_splits = op == "add_layernorm" and cols == 12288
+    plan = auto if auto_splits else split_plan(op, rows, cols)
     assert plan.family == lr.LR_FAMILY_SPLIT
-    if op not in ("layernorm", "add_layernorm"):
+    if not auto_splits:
         assert need == 0 and auto.family != lr.LR_FAMILY_SPLIT  # one launch is faster
     ws = torch.full((lr.lr_plan_workspace_bytes(plan, rows),), 0xFF, dtype=torch.uint8, device=DEV)
     inp = inputs(op, rows, cols, seed=cols + len(op))
@@ -117,7 +119,7 @@ def test_split_at_the_layernorm_workload_shape(op, cols):
     assert st2 == lr.LR_OK
     for k in got:
         assert np.array_equal(got[k].view(np.uint32), got2[k].view(np.uint32)), k
-    if op in ("layernorm", "add_layernorm"):  # the automatic plan with the queried workspace
+    if auto_splits:  # the automatic plan with the queried workspace
         assert need >= lr.lr_plan_workspace_bytes(plan, rows) > 0
         st3, got3 = run(op, inp, workspace=torch.empty(need, dtype=torch.uint8, device=DEV))
         assert st3 == lr.LR_OK
@@ -180,8 +182,8 @@ def test_split_layernorm_large_mean_small_spread():
     x = synth.normal_f32(9, 0, rows * cols, 1000.0, 1e-2).reshape(rows, cols)
     inp = {"x": x, "gamma": None, "beta": None}
     ref = oracle.layernorm(x, None, None, 1e-5)
-    ws = torch.empty(lr.lr_workspace_query("layernorm", rows, cols), dtype=torch.uint8, device=DEV)
-    st, split = run("layernorm", inp, workspace=ws)
+    p = split_plan("layernorm", rows, cols)
+    st, split = run("layernorm", inp, plan=p, workspace=workspace_for(p, rows))
     assert st == lr.LR_OK
     st, whole = run("layernorm", inp)
     assert st == lr.LR_OK
@@ -198,11 +200,12 @@ def test_split_layernorm_large_mean_small_spread():
 
 
 def test_workspace_beyond_the_plan_is_untouched_and_short_workspace_runs_unsplit():
-    rows, cols = 64, 12289
-    op = "layernorm"
+    rows, cols = 64, 12288
+    op = "add_layernorm"
     inp = inputs(op, rows, cols, seed=8)
     facts = lr.lr_device_facts_query()
-    plan = lr.lr_plan_for_device_ws(facts, op, rows, cols, "unordered_tree", 0)
+    plan = lr.lr_plan_for_device_ws(facts, op, rows, cols, "unordered_tree", 1)
+    assert plan.family == lr.LR_FAMILY_SPLIT
     need = lr.lr_plan_workspace_bytes(plan, rows)
     big = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device=DEV)
     st, got = run(op, inp, plan=plan, workspace=big)
@@ -237,9 +240,10 @@ def test_split_under_graph_replay():
     inp = inputs("layernorm", rows, cols, seed=2)
     x = torch.from_numpy(inp["x"]).to(DEV)
     g, b = torch.from_numpy(inp["gamma"]).to(DEV), torch.from_numpy(inp["beta"]).to(DEV)
-    ws = torch.empty(lr.lr_workspace_query("layernorm", rows, cols), dtype=torch.uint8, device=DEV)
+    p = split_plan("layernorm", rows, cols)
+    ws = workspace_for(p, rows)
     eager = torch.empty_like(x)
-    lr.check(lr.lr_layernorm_f32(x, g, b, eager, rows, cols, 1e-5, workspace=ws))
+    lr.check(lr.lr_layernorm_f32(x, g, b, eager, rows, cols, 1e-5, plan=p, workspace=ws))
     torch.cuda.synchronize()
     out = torch.full_like(x, float("nan"))
     graph = torch.cuda.CUDAGraph()
@@ -248,7 +252,7 @@ def test_split_under_graph_replay():
     with torch.cuda.stream(stream):
         with torch.cuda.graph(graph, stream=stream):
             lr.check(lr.lr_layernorm_f32(x, g, b, out, rows, cols, 1e-5, stream=torch.cuda.current_stream(),
-                                         workspace=ws))
+                                         plan=p, workspace=ws))
     torch.cuda.synchronize()
     for rep in range(4):
         out.fill_(float("nan"))
@@ -256,5 +260,5 @@ def test_split_under_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), rep
-        lr.check(lr.lr_layernorm_f32(x, g, b, eager, rows, cols, 1e-5, workspace=ws))
+        lr.check(lr.lr_layernorm_f32(x, g, b, eager, rows, cols, 1e-5, plan=p, workspace=ws))
         torch.cuda.synchronize()

@@ -219,15 +219,16 @@ def test_split_plan_legality():
 
 def test_workspace_plan_splits_few_long_rows_only():
     for op in OPS:
-        w = lr.lr_plan_for_device_ws(F, op, 64, 12289, "unordered_tree", 0)
-        if op in ("layernorm", "add_layernorm"):
-            assert w.family == lr.LR_FAMILY_SPLIT and w.splits >= 2 and w.blocks >= 256, (op, w)
-            assert lr.lr_plan_workspace_bytes(w, 64) == 64 * w.splits * 8
-            # the prior too (no measured entry at 48 rows)
-            v = lr.lr_plan_for_device_ws(F, op, 48, 16384, "unordered_tree", 1)
-            assert v.family == lr.LR_FAMILY_SPLIT and v.blocks >= 256, (op, v)
+        w = lr.lr_plan_for_device_ws(F, op, 64, 12288, "unordered_tree", 1)
+        v = lr.lr_plan_for_device_ws(F, op, 48, 16384, "unordered_tree", 1)  # the prior: no measured entry
+        if op == "add_layernorm":
+            for p, rows in ((w, 64), (v, 48)):
+                assert p.family == lr.LR_FAMILY_SPLIT and p.splits >= 2 and p.blocks >= 256, (op, p)
+                assert lr.lr_plan_workspace_bytes(p, rows) == rows * p.splits * 8
         else:  # one launch is faster for these
-            assert w.family != lr.LR_FAMILY_SPLIT, (op, w)
+            assert w.family != lr.LR_FAMILY_SPLIT and v.family != lr.LR_FAMILY_SPLIT, (op, w, v)
+        # measured: one launch at 64 x 12289, with or without a workspace
+        assert lr.lr_plan_for_device_ws(F, op, 64, 12289, "unordered_tree", 0).family != lr.LR_FAMILY_SPLIT
         # enough rows to fill the device, or rows too short to be worth a
         # second launch: no split
         for rows, cols in [(768, 6144), (4096, 32000), (37, 1537), (64, 512)]:
