@@ -401,7 +401,10 @@ static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_
         // (the smallest power of two lanes from 4 to 32 that covers the row)
         int L = 4;
         while (L < nv) L *= 2;
-        const int waves = aligned ? 1 : 4;
+        // one wave per workgroup on aligned rows, four on misaligned rows and
+        // for cross-entropy (on MI355X: 262144 x 32 10.1 us against 10.6,
+        // 1048576 x 16 18.6 against 19.0)
+        const int waves = aligned && op != LR_OP_CROSS_ENTROPY ? 1 : 4;
         lr_plan p = make_plan(LR_FAMILY_CACHE, 1, waves * (kWave / L), 1, rows, cols, op, aligned, 0, L);
         if (validate_plan(f, op, rows, cols, policy, aligned, &p) == LR_OK) return p;
     }
