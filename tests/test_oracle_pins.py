@@ -597,3 +597,58 @@ def test_fold_replay_rows_are_independent():
     for r in range(5):
         one = oracle.layernorm_fold_f32(inp["x"][r:r + 1], inp["gamma"], inp["beta"], 1e-5)
         assert np.array_equal(one[0], full[r])
+
+
+# --------------------------------------------------------------------------
+# the ordered replays' FP32 steps after the fold, against hand-worked values
+# (tests/golden/ordered_post_fold.json: the mean as acc / cols, IEEE division
+# and square root, (x * r) * gamma, ((x - mu) * r) * gamma + beta, each
+# rounded on its own; "TIRx Metal reduction lowering", section 1)
+# --------------------------------------------------------------------------
+
+GOLDEN_POST_FOLD = os.path.join(os.path.dirname(__file__), "golden", "ordered_post_fold.json")
+
+
+def _post_fold_cases():
+    with open(GOLDEN_POST_FOLD) as f:
+        return json.load(f)["cases"]
+
+
+def _post_fold_replays(case):
+    """Every FP32 replay of the case's operation: the fold_left replay and the
+    replays under each ordered policy (the rows' sums are exact integers, so
+    the order cannot change them)."""
+    x = np.array([case["x"]], dtype=np.float32)
+    g = None if case.get("gamma") is None else np.array(case["gamma"], dtype=np.float32)
+    eps = case["eps"]
+    if case["op"] == "rmsnorm":
+        yield "fold_f32", oracle.rmsnorm_fold_f32(x, g, eps)
+        for pol in ORDERED:
+            yield pol, oracle.rmsnorm_ordered_f32(x, g, eps, pol)
+    else:
+        b = None if case.get("beta") is None else np.array(case["beta"], dtype=np.float32)
+        yield "fold_f32", oracle.layernorm_fold_f32(x, g, b, eps)
+        for pol in ORDERED:
+            yield pol, oracle.layernorm_ordered_f32(x, g, b, eps, pol)
+
+
+@pytest.mark.parametrize("case", _post_fold_cases(), ids=lambda c: c["name"])
+def test_ordered_post_fold_golden(case):
+    want = np.array(case["expected"], dtype=np.float32).view(np.uint32)
+    for name, y in _post_fold_replays(case):
+        got = y[0].view(np.uint32)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (name, case["name"], bad[:4], y[0][bad[:4]])
+
+
+def test_ordered_post_fold_golden_values_are_the_stated_mantissas():
+    """The decimal values in the golden file are the m * 2^e forms its
+    derivations give (read here as exact binary fractions, not recomputed)."""
+    cases = {c["name"]: c for c in _post_fold_cases()}
+    ln = np.array(cases["layernorm_scale_gamma_beta_each_rounded"]["expected"], dtype=np.float32)
+    assert float(ln[0]) == 97867104 * 2.0 ** -25
+    assert float(ln[1]) == -78293680 * 2.0 ** -25
+    assert float(ln[2]) == 0.0
+    assert all(abs(float(v)) == 11184811 * 2.0 ** -25 for v in ln[3:])
+    rms = cases["rmsnorm_scales_then_applies_gamma"]
+    assert rms["expected"] == rms["gamma"]
