@@ -35,6 +35,16 @@
  * Errors.   Every argument is validated before any HIP call; nothing falls
  *           back to the CPU.  An explicit plan that cannot be realised
  *           returns LR_ERR_UNREALIZABLE_PLAN; it is never clamped.
+ * Values.   Inputs are finite, with one exception: softmax and cross-entropy
+ *           rows may hold -infinity (masked positions) as long as every
+ *           row keeps at least one finite element; a masked element's
+ *           softmax output is +0 and it adds nothing to the sum.  A row of
+ *           nothing but -infinity, NaN, +infinity, or a non-finite value
+ *           in any other operation is outside the contract: no error is
+ *           reported and the result is unspecified (it may differ between
+ *           policies and plans).  For lr_row_minmax_f32 in particular, a
+ *           NaN element may be skipped or returned depending on the
+ *           policy.
  * Threads.  All entry points are thread-safe.
  * Policy.   See lr_reduction_policy below: LR_UNORDERED_TREE lets every
  *           add fold be reassociated; the three ordered policies fix the

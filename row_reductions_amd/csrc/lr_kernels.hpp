@@ -361,16 +361,19 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
 #pragma unroll
         for (int c = 0; c < NCH; ++c) m = fmax2(fmax2(m, fmax2(v[c].x, v[c].y)), fmax2(v[c].z, v[c].w));
         m = group_allreduce<MaxOp, LW>(m);
+        // a wave whose elements are all -inf (masked, or past the row's end)
+        // shifts by 0 instead of by its maximum: its exponentials are then
+        // exp(-inf) = 0 (its outputs +0, not -inf * 0), and it brings
+        // (-inf, 0) to the merge
+        const float mm = (m == -INFINITY) ? 0.0f : m;
         float s = 0.0f;
-        if (m != -INFINITY) {  // a wave with no element of the row keeps (-inf, 0)
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                v[c].x = fast_exp(v[c].x - m);
-                v[c].y = fast_exp(v[c].y - m);
-                v[c].z = fast_exp(v[c].z - m);
-                v[c].w = fast_exp(v[c].w - m);
-                s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
-            }
+        for (int c = 0; c < NCH; ++c) {
+            v[c].x = fast_exp(v[c].x - mm);
+            v[c].y = fast_exp(v[c].y - mm);
+            v[c].z = fast_exp(v[c].z - mm);
+            v[c].w = fast_exp(v[c].w - mm);
+            s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
         }
         s = group_allreduce<AddOp, LW>(s);
         const MaxSum ms = team_maxsum(m, s, red[0], red[1], S, t);
@@ -482,7 +485,8 @@ k_cache_narrow(const KArgs a) {
 // ===========================================================================
 // STREAM family: the row is walked in trips of U chunks per worker; passes
 // that need it again reload it.  Softmax and cross-entropy fold (max,
-// sum of exp) online in one pass and merge the per-worker pairs at the end.
+// sum of exp) online in one pass (Milakov and Gimelshein's online normaliser)
+// and merge the per-worker pairs at the end.
 // ===========================================================================
 template <int OP, bool AL>
 __device__ __forceinline__ void load_trip(float4 (&v)[kStreamUnroll], const float4* xa, BufRes rr, int k0,
@@ -533,12 +537,15 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 tm = fmax2(fmax2(tm, fmax2(v[u].x, v[u].y)), fmax2(v[u].z, v[u].w));
-            s *= fast_exp(m - tm);  // m = -inf on the first trip: s is 0 anyway
+            // while every element so far is -inf (masked), shift by 0: the
+            // exponentials are then exp(-inf) = 0 and s stays 0
+            const float mm = (tm == -INFINITY) ? 0.0f : tm;
+            s *= fast_exp(m - mm);  // m = -inf until a finite element: s is 0 anyway
             m = tm;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                s += (fast_exp(v[u].x - m) + fast_exp(v[u].y - m)) +
-                     (fast_exp(v[u].z - m) + fast_exp(v[u].w - m));
+                s += (fast_exp(v[u].x - mm) + fast_exp(v[u].y - mm)) +
+                     (fast_exp(v[u].z - mm) + fast_exp(v[u].w - mm));
         }
         const float M = team_reduce<MaxOp>(m, red[0], S, t);
         // a worker with no elements has m = -inf and s = 0
