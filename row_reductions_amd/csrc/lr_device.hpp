@@ -237,9 +237,11 @@ __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_r
 
 // Softmax state over a row team with one exchange: every wave brings its
 // own (max m_w, sum of exp(x - m_w)) pair, lane 0 publishes it, one workgroup
-// barrier, then every wave merges the S pairs ("TIRx Metal reduction
-// lowering", section 1, the online softmax state): M = max_w m_w,
-// s = sum_w s_w exp(m_w - M).  A wave with no element of the row brings
+// barrier, then every wave merges the S pairs with the (max, sum of
+// exponentials) merge of Milakov and Gimelshein's online normaliser
+// ("Online normalizer calculation for softmax", 2018; the pages compose max,
+// sum of exp and the division, section 1, but give no merge):
+// M = max_w m_w, s = sum_w s_w exp(m_w - M).  A wave with no element of the row brings
 // (-inf, 0).  `sm`, `ss`: this round's LDS arrays of Q*S floats.
 struct MaxSum {
     float m, s;

@@ -20,8 +20,9 @@
 //
 // Merges (lane g of a wave holds partial g, the wave tree combines them, so
 // every wave of a row gets the same bits):
-//   max / sum of exp ("TIRx Metal reduction lowering", section 1, the online
-//   softmax state): M = max_g m_g, s = sum_g s_g exp(m_g - M);
+//   max / sum of exp (the merge of Milakov and Gimelshein, "Online
+//   normalizer calculation for softmax", 2018): M = max_g m_g,
+//   s = sum_g s_g exp(m_g - M);
 //   LayerNorm (section 5.1 statistics, merged as Chan, Golub and LeVeque's
 //   pairwise update): mean = sum_g n_g mean_g / cols,
 //   M2 = sum_g (M2_g + n_g (mean_g - mean)^2), var = M2 / cols.
