@@ -9,10 +9,15 @@ the L2s), so each launch streams its tensor from HBM ("cold").
 
 Printed: one JSON line with throughput (GB/s of algorithmic bytes = tensor
 read + tensor write per op), per-op microseconds, the roofline record of the
-dominant kernel (its average launch duration: HIP events around a batch of
-back-to-back cold launches of that kernel alone), the oracle's CPU baseline
-and, as context,
-warm-cache and cross-entropy 4096 x 32000 figures.
+dominant kernel, the oracle's CPU baseline and, as context, warm-cache and
+cross-entropy 4096 x 32000 figures.
+
+Per-op times follow the measurement protocol of the pages' whole-launch cost
+notes, whatever --steps is: at least 200 ms of warm-up launches, then nine
+samples, each a batch of back-to-back launches of that op alone lasting at
+least 30 ms between two HIP events on the launch stream; the median is
+reported with the [min, max] range.  The roofline's average launch duration
+is that median.
 
     python bench.py [--steps K] [--warmup W] [--warm] [--no-cpu-baseline]
                     [--no-extra] [--copy-probe]
@@ -41,6 +46,7 @@ PAGES_M1MAX_STEP_US = 57.414 + 60.753 + 75.251
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_768x6144.json")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "kernel_trace_768x6144.json")
 
 
 def traffic_bytes(lr, op: str):
@@ -53,6 +59,71 @@ def traffic_bytes(lr, op: str):
     kernel = profiling.kernel_name(lr.OPS[op], plan, True, params)
     rec = profiling.lookup(TRAFFIC_SUMMARY, op, kernel)
     return None if rec is None else round(rec["traffic_bytes"])
+
+
+WARMUP_MS = 200.0
+SAMPLE_MS = 30.0
+SAMPLES = 9
+
+
+def time_batches(torch, stream, launch, samples: int = SAMPLES, sample_ms: float = SAMPLE_MS,
+                 warmup_ms: float = WARMUP_MS, calib: int = 200) -> dict:
+    """Median, minimum and maximum microseconds per launch of `launch(i)`
+    (i = running launch index, which picks the buffer set) over `samples`
+    batches of back-to-back launches, each at least `sample_ms` long, after
+    at least `warmup_ms` of warm-up launches.  Each batch starts with a few
+    untimed launches, so that the GPU is busy when the start event is
+    reached and no host-side gap enters the batch."""
+    i = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warmup_ms:
+        for _ in range(min(64, calib)):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+    # launches per batch from a short calibration batch
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(calib):
+        launch(i)
+        i += 1
+    z.record(stream)
+    torch.cuda.synchronize()
+    est_us = a.elapsed_time(z) * 1e3 / calib
+    n = max(calib, int(sample_ms * 1e3 / est_us * 1.1) + 1)
+    vals = []
+    for _ in range(samples):
+        for _ in range(8):
+            launch(i)
+            i += 1
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            launch(i)
+            i += 1
+        z.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(z)
+        vals.append(ms * 1e3 / n)
+    vals.sort()
+    return {"median": vals[len(vals) // 2], "min": vals[0], "max": vals[-1], "launches_per_sample": n,
+            "sample_ms": round(vals[len(vals) // 2] * n / 1e3, 2)}
+
+
+def trace_fraction(lr, op: str, nbytes: int) -> dict:
+    """The kernel-trace average duration of `op`'s kernel instance from the
+    committed rocprofv3 summary, and the roofline fraction it gives; nulls
+    when the kernels changed since the trace was taken or the summary holds
+    another instance than this plan launches."""
+    from row_reductions_amd import profiling
+    plan = lr.lr_plan_query(op, ROWS, COLS, "unordered_tree")
+    params = {"softmax": 0, "rmsnorm": 1, "layernorm": 1}[op]
+    kernel = profiling.kernel_name(lr.OPS[op], plan, True, params)
+    rec = profiling.lookup(TRACE_SUMMARY, op, kernel)
+    if rec is None:
+        return {"trace_us": None, "frac_trace": None}
+    return {"trace_us": round(rec["avg_us"], 3), "frac_trace": round(nbytes / (rec["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "trace_dispatches": rec["dispatches"]}
 
 
 def op_bytes(rows: int, cols: int) -> int:
@@ -153,19 +224,10 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / K
     gpu_ms_per_step = t_start.elapsed_time(t_end) / K
 
-    # per-kernel average launch duration: each op alone, K back-to-back cold
-    # launches on the same stream, HIP events around the batch
-    per_op_us = {}
-    for op in OPS:
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for i in range(10):
-            launch(op, i)
-        a.record(stream)
-        for i in range(K):
-            launch(op, i)
-        z.record(stream)
-        torch.cuda.synchronize()
-        per_op_us[op] = a.elapsed_time(z) * 1e3 / K
+    # per-op launch duration: each op alone, the pages' protocol (warm-up of
+    # at least 200 ms, nine batches of at least 30 ms, median and range)
+    per_op = {op: time_batches(torch, stream, lambda i, op=op: launch(op, i)) for op in OPS}
+    per_op_us = {op: per_op[op]["median"] for op in OPS}
 
     b = op_bytes(ROWS, COLS)
     step_bytes = b * len(OPS)
@@ -220,6 +282,10 @@ def main():
                                 "(57.414/60.753/75.251 us); context, not a target",
         },
         "us_per_op": {op: round(per_op_us[op], 3) for op in OPS},
+        "us_per_op_range": {op: [round(per_op[op]["min"], 3), round(per_op[op]["max"], 3)] for op in OPS},
+        "per_op_protocol": (f"median of {SAMPLES} batches of >= {SAMPLE_MS:.0f} ms of back-to-back cold launches "
+                            f"({per_op[OPS[0]]['launches_per_sample']} launches of {OPS[0]} per batch) after "
+                            f">= {WARMUP_MS:.0f} ms of warm-up, HIP events on the launch stream"),
         "single_call_us": single,
         "gbps_per_op": {op: round(gbps[op], 1) for op in OPS},
         "pct_of_hbm_peak_per_op": {op: round(100 * gbps[op] / HBM_PEAK_GBS, 2) for op in OPS},
@@ -234,6 +300,10 @@ def main():
             "traffic": traffic_bytes(lr, dominant),
             "bytes_per_launch": b,
             "avg_launch_us": round(per_op_us[dominant], 3),
+            "avg_launch_us_range": [round(per_op[dominant]["min"], 3), round(per_op[dominant]["max"], 3)],
+            "gate": "frac (back-to-back launches, event-timed median); frac_trace is the kernel-trace duration "
+                    "of the committed rocprofv3 profile, where every dispatch starts on an idle GPU",
+            **trace_fraction(lr, dominant, b),
         },
     }
 
@@ -241,32 +311,17 @@ def main():
     if not args.no_extra:
         extra = {}
         if not args.warm:
-            n = 400
             for op in OPS:
-                for i in range(20):
-                    launch(op, 0)
-                torch.cuda.synchronize()
-                a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for i in range(n):
-                    launch(op, 0)
-                z.record(stream)
-                torch.cuda.synchronize()
-                us = a.elapsed_time(z) * 1e3 / n
-                extra[f"{op}_768x6144_warm"] = {"us_per_op": round(us, 3), "gbps": round(b / us / 1e3, 1)}
+                t = time_batches(torch, stream, lambda i, op=op: launch(op, 0), samples=5)
+                extra[f"{op}_768x6144_warm"] = {"us_per_op": round(t["median"], 3),
+                                                "range": [round(t["min"], 3), round(t["max"], 3)],
+                                                "gbps": round(b / t["median"] / 1e3, 1)}
         # the deterministic ordered_tree policy on the same step (cold)
         for op in OPS:
-            for i in range(10):
-                launch(op, i, lr.LR_ORDERED_TREE)
-            torch.cuda.synchronize()
-            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for i in range(400):
-                launch(op, i, lr.LR_ORDERED_TREE)
-            z.record(stream)
-            torch.cuda.synchronize()
-            us = a.elapsed_time(z) * 1e3 / 400
-            extra[f"{op}_768x6144_ordered_tree_cold"] = {"us_per_op": round(us, 3), "gbps": round(b / us / 1e3, 1)}
+            t = time_batches(torch, stream, lambda i, op=op: launch(op, i, lr.LR_ORDERED_TREE), samples=5)
+            extra[f"{op}_768x6144_ordered_tree_cold"] = {"us_per_op": round(t["median"], 3),
+                                                         "range": [round(t["min"], 3), round(t["max"], 3)],
+                                                         "gbps": round(b / t["median"] / 1e3, 1)}
         extra.update(add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets))
         extra.update(small_configs_graph(lr, synth, torch, dev))
         ce = synth.cross_entropy_inputs(4096, 32000, seed=0)
@@ -275,23 +330,17 @@ def main():
         clab = torch.from_numpy(ce["labels"]).to(dev)
         closs = torch.empty(4096, device=dev)
         del ce
-        n = 100
-        for i in range(10):
+        for i in range(4):
             lr.check(lr.lib.lr_cross_entropy_f32(cx[i % 2].data_ptr(), clab.data_ptr(), closs.data_ptr(),
                                                  4096, 32000, 0, sh))
-        torch.cuda.synchronize()
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(n):
-            lr.lib.lr_cross_entropy_f32(cx[i % 2].data_ptr(), clab.data_ptr(), closs.data_ptr(), 4096, 32000,
-                                        0, sh)
-        z.record(stream)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(z) * 1e3 / n
+        t = time_batches(torch, stream, lambda i: lr.lib.lr_cross_entropy_f32(
+            cx[i % 2].data_ptr(), clab.data_ptr(), closs.data_ptr(), 4096, 32000, 0, sh), samples=5)
+        us = t["median"]
         cb = ce_bytes(4096, 32000)
         p = lr.lr_plan_query("cross_entropy", 4096, 32000)
         extra["cross_entropy_4096x32000_cold"] = {
-            "us_per_op": round(us, 3), "gbps": round(cb / us / 1e3, 1),
+            "us_per_op": round(us, 3), "range": [round(t["min"], 3), round(t["max"], 3)],
+            "gbps": round(cb / us / 1e3, 1),
             "pct_of_hbm_peak": round(100 * cb / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": cb,
             "plan": {k: v for k, v in p.as_dict().items() if k in (
                 "family", "waves_per_row", "rows_per_block", "chunks_per_lane", "threads_per_block")}}
@@ -304,18 +353,13 @@ def main():
             ("row_minmax_4096x32000_cold",
              lambda i: lr.lib.lr_row_minmax_f32(cx[i % 2].data_ptr(), rmin.data_ptr(), rmax.data_ptr(), 4096,
                                                 32000, 0, sh), 8)):
-            for i in range(10):
+            for i in range(4):
                 lr.check(fn(i), name)
-            torch.cuda.synchronize()
-            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for i in range(n):
-                fn(i)
-            z.record(stream)
-            torch.cuda.synchronize()
-            us = a.elapsed_time(z) * 1e3 / n
+            t = time_batches(torch, stream, fn, samples=5)
+            us = t["median"]
             rb = 4096 * 32000 * 4 + 4096 * outb
-            extra[name] = {"us_per_op": round(us, 3), "gbps": round(rb / us / 1e3, 1),
+            extra[name] = {"us_per_op": round(us, 3), "range": [round(t["min"], 3), round(t["max"], 3)],
+                           "gbps": round(rb / us / 1e3, 1),
                            "pct_of_hbm_peak": round(100 * rb / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": rb}
         del cx
         # narrow rows (several rows per wave): 262144 x 64, four rotating
@@ -335,17 +379,12 @@ def main():
                                              1e-6, 1, sh))):
             for i in range(8):
                 lr.check(fn(i), name)
-            torch.cuda.synchronize()
-            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for i in range(n):
-                fn(i)
-            z.record(stream)
-            torch.cuda.synchronize()
-            us = a.elapsed_time(z) * 1e3 / n
+            t = time_batches(torch, stream, fn, samples=5)
+            us = t["median"]
             nbytes = op_bytes(262144, 64)
             p = lr.lr_plan_query(op, 262144, 64, pol)
-            extra[name] = {"us_per_op": round(us, 3), "gbps": round(nbytes / us / 1e3, 1),
+            extra[name] = {"us_per_op": round(us, 3), "range": [round(t["min"], 3), round(t["max"], 3)],
+                           "gbps": round(nbytes / us / 1e3, 1),
                            "pct_of_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": nbytes,
                            "plan": {k: v for k, v in p.as_dict().items() if k in (
                                "family", "lanes_per_row", "rows_per_block", "chunks_per_lane", "threads_per_block")}}
@@ -411,16 +450,11 @@ def small_configs_graph(lr, synth, torch, dev) -> dict:
                 for _ in range(n):
                     fn(torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(5):
-            graph.replay()
-        z.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(z) * 1e3 / (5 * n)
-        out[f"{name}_graph"] = {"us_per_op": round(us, 3), "gbps": round(nbytes / us / 1e3, 1)}
+        # one "launch" of the protocol is one replay of n kernels
+        t = time_batches(torch, torch.cuda.current_stream(), lambda i: graph.replay(), samples=5, calib=8)
+        us = t["median"] / n
+        out[f"{name}_graph"] = {"us_per_op": round(us, 3), "range": [round(t["min"] / n, 3), round(t["max"] / n, 3)],
+                                "gbps": round(nbytes / us / 1e3, 1)}
     return out
 
 
@@ -437,7 +471,6 @@ def add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets) -> dict:
     g = torch.from_numpy(inp["gamma"]).to(dev)
     b = torch.from_numpy(inp["beta"]).to(dev)
     out = {}
-    n = 400
     tb = ROWS * COLS * 4
     for with_sum in (False, True):
         def launch(i):
@@ -447,19 +480,12 @@ def add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets) -> dict:
                                              ROWS, COLS, EPS["layernorm"], 0, sh)
             if st != 0:
                 raise lr.LrError(st, "add_layernorm")
-        for i in range(20):
-            launch(i)
-        torch.cuda.synchronize()
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(n):
-            launch(i)
-        z.record(stream)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(z) * 1e3 / n
+        t = time_batches(torch, stream, launch, samples=5)
+        us = t["median"]
         moved = (4 if with_sum else 3) * tb
         key = "add_layernorm_768x6144_cold" + ("_with_sum" if with_sum else "")
-        out[key] = {"us_per_op": round(us, 3), "gbps": round(moved / us / 1e3, 1),
+        out[key] = {"us_per_op": round(us, 3), "range": [round(t["min"], 3), round(t["max"], 3)],
+                    "gbps": round(moved / us / 1e3, 1),
                     "pct_of_hbm_peak": round(100 * moved / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": moved}
     del xs, rs, ys, ss
     return out
@@ -477,20 +503,26 @@ def _cpu_model() -> str:
 
 
 def cpu_baseline(soft, rms, ln, budget_s: float) -> dict:
-    """The double-precision oracle, unmodified, on the same 768x6144 inputs.
-    Rows are split over host threads (the C oracle releases the GIL); the
-    whole three-op workload is repeated until `budget_s` seconds are used."""
+    """The double-precision oracle, unmodified, on the same 768x6144 inputs,
+    timed two ways: rows split over the host threads this process may use
+    (at most 16, the CPU share of one GPU; the C oracle releases the GIL),
+    the whole three-op workload repeated until `budget_s` seconds are used;
+    and on one thread over the first 96 rows of each op for up to
+    budget_s / 2 seconds, scaled to the same GB/s unit."""
     import concurrent.futures as cf
 
     import numpy as np
 
     import oracle
 
-    cores = min(16, os.cpu_count() or 1)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    cores = max(1, min(16, avail))
     chunks = np.array_split(np.arange(ROWS), cores)
 
-    def run_rows(idx):
-        lo, hi = int(idx[0]), int(idx[-1]) + 1
+    def run_rows(lo, hi):
         oracle.softmax(soft["x"][lo:hi])
         oracle.rmsnorm(rms["x"][lo:hi], rms["gamma"], EPS["rmsnorm"])
         oracle.layernorm(ln["x"][lo:hi], ln["gamma"], ln["beta"], EPS["layernorm"])
@@ -499,13 +531,26 @@ def cpu_baseline(soft, rms, ln, budget_s: float) -> dict:
     with cf.ThreadPoolExecutor(max_workers=cores) as ex:
         t0 = time.perf_counter()
         while True:
-            list(ex.map(run_rows, chunks))
+            list(ex.map(lambda idx: run_rows(int(idx[0]), int(idx[-1]) + 1), chunks))
             reps += 1
             el = time.perf_counter() - t0
             if el >= budget_s or reps >= 1000:
                 break
     step_s = el / reps
     step_bytes = op_bytes(ROWS, COLS) * len(OPS)
+
+    # one thread, a bounded sample: the first 96 rows of each op
+    srows = 96
+    reps1 = 0
+    t0 = time.perf_counter()
+    while True:
+        run_rows(0, srows)
+        reps1 += 1
+        el1 = time.perf_counter() - t0
+        if el1 >= budget_s / 2 or reps1 >= 1000:
+            break
+    one_s = el1 / reps1
+    one_bytes = op_bytes(srows, COLS) * len(OPS)
     return {
         "value": round(step_bytes / step_s / 1e9, 3),
         "unit": "GB/s",
@@ -513,6 +558,11 @@ def cpu_baseline(soft, rms, ln, budget_s: float) -> dict:
         "kind": "oracle",
         "sample": f"full workload (softmax+RMSNorm+LayerNorm 768x6144), {reps} repetitions in {el:.1f} s, "
                   f"rows split over {cores} threads; {step_s * 1e3:.2f} ms per step",
+        "single_thread": {"value": round(one_bytes / one_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+                          "sample": f"first {srows} rows of each op, {reps1} repetitions in {el1:.1f} s; "
+                                    f"{one_s * 1e3 * ROWS / srows:.1f} ms per full step (scaled)"},
+        "nproc": os.cpu_count(),
+        "affinity_cores": avail,
         "cpu": _cpu_model(),
     }
 

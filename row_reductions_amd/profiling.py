@@ -88,6 +88,25 @@ def traffic(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
     return out
 
 
+def trace(trace_csv: str, kernels: list[str] | None = None) -> dict:
+    """Per-kernel dispatch count and average / median / minimum / maximum
+    duration in microseconds from a `rocprofv3 --kernel-trace` CSV, for the
+    row-reduction kernels (or the named ones)."""
+    durs = defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if (kernels and name not in kernels) or (not kernels and kernel_op(name) is None):
+                continue
+            durs[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = {"csrc_sha256": csrc_hash(), "kernels": {}}
+    for name, d in durs.items():
+        d.sort()
+        out["kernels"][name] = {"op": kernel_op(name), "dispatches": len(d), "avg_us": sum(d) / len(d),
+                                "median_us": d[len(d) // 2], "min_us": d[0], "max_us": d[-1]}
+    return out
+
+
 def kernel_name(op_index: int, plan, aligned: bool, param_mode: int) -> str | None:
     """The demangled name of the kernel instance a CACHE or STREAM plan
     launches (param_mode: 0 no gamma/beta, 1 all present, 2 some)."""
@@ -124,10 +143,23 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     t.add_argument("--out", required=True)
+    tr = sub.add_parser("trace")
+    tr.add_argument("--trace", required=True, help="rocprofv3 kernel-trace CSV")
+    tr.add_argument("--command", default="", help="the profiling command, recorded in the summary")
+    tr.add_argument("--out", required=True)
     sub.add_parser("hash")
     a = ap.parse_args(argv)
     if a.cmd == "hash":
         print(csrc_hash())
+        return 0
+    if a.cmd == "trace":
+        s = trace(a.trace)
+        s["command"] = a.command
+        with open(a.out, "w") as f:
+            json.dump(s, f, indent=1)
+        for name, rec in s["kernels"].items():
+            print(f"{rec['op']:14s} {rec['dispatches']:7d} dispatches  avg {rec['avg_us']:8.3f} us  "
+                  f"median {rec['median_us']:8.3f} us  {name}")
         return 0
     s = traffic(a.fetch, a.write, a.copy_bytes)
     s["command"] = a.command
