@@ -13,10 +13,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.   All tensor pointers are DEVICE pointers owned by the caller.  The
- *           library allocates no device memory, keeps no device state and
- *           never reads or writes outside the ranges described per call
- *           (the SPLIT family's partials go to a workspace the caller
- *           passes to lr_run_f32).
+ *           library allocates no device memory and never reads or writes
+ *           outside the ranges described per call (the SPLIT family's
+ *           partials go to a workspace the caller passes to lr_run_f32, or
+ *           to the one device array per GPU that lr_run_f32_noalloc owns,
+ *           the library's only device state).
  *           FP32 pointers must be 4-byte aligned and the int64 label pointer
  *           8-byte aligned (else LR_ERR_MISALIGNED); 16-byte alignment is not
  *           required (misaligned rows take a guarded path).
@@ -347,6 +348,29 @@ typedef struct lr_tensors {
 lr_status lr_run_f32(lr_op op, const lr_tensors* tensors, int64_t rows, int64_t cols, float eps,
                      lr_reduction_policy policy, const lr_plan* plan, void* workspace,
                      uint64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the device array lr_run_f32_noalloc uses in place of a workspace
+ * (one copy per GPU, held until the process ends): room for 131072 split-row
+ * partials, e.g. 2048 rows cut into 64 segments. */
+#define LR_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/* lr_run_f32 for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as lr_run_f32 with a workspace of
+ * LR_NOALLOC_SCRATCH_BYTES bytes, except that the workspace is a device array
+ * the library owns, one per GPU (its address on the current device is looked
+ * up on the first call there).  The call allocates and frees nothing.
+ *   - An explicit SPLIT plan whose partials (lr_plan_workspace_bytes) exceed
+ *     LR_NOALLOC_SCRATCH_BYTES returns LR_ERR_WORKSPACE before any launch;
+ *     the automatic plan splits rows only when its partials fit.
+ *   - Every call on one GPU shares that GPU's array.  Each call writes every
+ *     partial it reads, so nothing carries over, but calls whose work
+ *     overlaps in time on one GPU (different streams or host threads) race
+ *     on the array: order them on one stream.
+ *   - `stream` must belong to the current device.  LR_ERR_HIP if the array's
+ *     address cannot be looked up. */
+lr_status lr_run_f32_noalloc(lr_op op, const lr_tensors* tensors, int64_t rows, int64_t cols, float eps,
+                             lr_reduction_policy policy, const lr_plan* plan, hipStream_t stream);
 
 /* Workspace bytes lr_run_f32's automatic plan uses for this problem on the
  * current device with a workspace available (0 when it does not split):

@@ -134,6 +134,7 @@ def _load():
         "lr_plan_validate": [PF, I32, I64, I64, I32, I32, PP],
         "lr_coverage_check": [PP, I64, I64, I32, P],
         "lr_run_f32": [I32, ctypes.POINTER(LrTensors), I64, I64, F32, I32, PP, P, ctypes.c_uint64, P],
+        "lr_run_f32_noalloc": [I32, ctypes.POINTER(LrTensors), I64, I64, F32, I32, PP, P],
         "lr_workspace_query": [I32, I64, I64, I32, ctypes.POINTER(ctypes.c_uint64)],
         "lr_plan_for_device_ws": [PF, I32, I64, I64, I32, I32, PP],
     }
@@ -213,6 +214,17 @@ def lr_run_f32(op, rows, cols, eps=0.0, policy=LR_UNORDERED_TREE, plan=None, wor
     return lib.lr_run_f32(_op(op), ctypes.byref(t), rows, cols, eps, _policy(policy),
                           None if plan is None else ctypes.byref(plan), _ptr(workspace),
                           _nbytes(workspace, workspace_bytes), _stream(stream))
+
+
+def lr_run_f32_noalloc(op, rows, cols, eps=0.0, policy=LR_UNORDERED_TREE, plan=None, stream=None, **tensors) -> int:
+    """lr_run_f32_noalloc: lr_run_f32 with the library's own device array in
+    place of a workspace (LR_NOALLOC_SCRATCH_BYTES bytes per GPU)."""
+    unknown = set(tensors) - set(TENSOR_FIELDS)
+    if unknown:
+        raise TypeError("unknown tensor arguments: %s" % sorted(unknown))
+    t = LrTensors(**{k: _ptr(v) for k, v in tensors.items()})
+    return lib.lr_run_f32_noalloc(_op(op), ctypes.byref(t), rows, cols, eps, _policy(policy),
+                                  None if plan is None else ctypes.byref(plan), _stream(stream))
 
 
 def lr_workspace_query(op, rows, cols, policy=LR_UNORDERED_TREE) -> int:

@@ -41,6 +41,7 @@ EXTRA.update({f"k_tree_{op}.hip": ORDERED_FLAGS for op in TREE_OPS})
 SOURCES = [
     "lr_abi.cpp",
     "lr_planner.cpp",
+    "lr_noalloc.hip",
     "k_softmax.hip",
     "k_rmsnorm.hip",
     "k_layernorm.hip",

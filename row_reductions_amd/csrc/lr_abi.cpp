@@ -401,9 +401,12 @@ lr_status lr_row_minmax_f32_with_plan(const float* x, float* mins, float* maxs, 
     return lr::run(c, plan, stream);
 }
 
-lr_status lr_run_f32(lr_op op, const lr_tensors* t, int64_t rows, int64_t cols, float eps,
-                     lr_reduction_policy policy, const lr_plan* plan, void* workspace, uint64_t workspace_bytes,
-                     hipStream_t stream) {
+namespace {
+
+// The call of lr_run_f32 (no workspace yet): members the operation does not
+// use must be NULL.
+lr_status run_call(lr_op op, const lr_tensors* t, int64_t rows, int64_t cols, float eps,
+                   lr_reduction_policy policy, lr::Call* out) {
     if (t == nullptr) return LR_ERR_NULL_POINTER;
     if (op < LR_OP_SOFTMAX || op > LR_OP_ROW_MINMAX) return LR_ERR_INVALID_ARGUMENT;
     // members the operation does not use must be NULL
@@ -421,8 +424,39 @@ lr_status lr_run_f32(lr_op op, const lr_tensors* t, int64_t rows, int64_t cols, 
     c.sums = t->sums;
     c.mins = t->mins;
     c.maxs = t->maxs;
+    *out = c;
+    return LR_OK;
+}
+
+}  // namespace
+
+lr_status lr_run_f32(lr_op op, const lr_tensors* t, int64_t rows, int64_t cols, float eps,
+                     lr_reduction_policy policy, const lr_plan* plan, void* workspace, uint64_t workspace_bytes,
+                     hipStream_t stream) {
+    Call c{};
+    const lr_status st = run_call(op, t, rows, cols, eps, policy, &c);
+    if (st != LR_OK) return st;
     c.workspace = workspace;
     c.workspace_bytes = workspace_bytes;
+    return lr::run(c, plan, stream);
+}
+
+lr_status lr_run_f32_noalloc(lr_op op, const lr_tensors* t, int64_t rows, int64_t cols, float eps,
+                             lr_reduction_policy policy, const lr_plan* plan, hipStream_t stream) {
+    Call c{};
+    lr_status st = run_call(op, t, rows, cols, eps, policy, &c);
+    if (st != LR_OK) return st;
+    // every argument is checked before the array's address is looked up
+    st = lr::validate_call(c);
+    if (st != LR_OK) return st;
+    if (c.rows == 0) return LR_OK;
+    if (plan != nullptr && lr_plan_workspace_bytes(plan, rows) > (uint64_t)LR_NOALLOC_SCRATCH_BYTES)
+        return LR_ERR_WORKSPACE;
+    void* ws = nullptr;
+    st = lr::noalloc_scratch(&ws);
+    if (st != LR_OK) return st;
+    c.workspace = ws;
+    c.workspace_bytes = LR_NOALLOC_SCRATCH_BYTES;
     return lr::run(c, plan, stream);
 }
 

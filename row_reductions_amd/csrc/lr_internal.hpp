@@ -94,6 +94,10 @@ hipError_t launch_tree_add_layernorm(const KArgs& a, const lr_plan& p, bool alig
 hipError_t launch_tree_row_sum(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_tree_row_minmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 
+// The current device's address of lr_run_f32_noalloc's device array
+// (lr_noalloc.hip), looked up on the first call on that device.
+lr_status noalloc_scratch(void** out);
+
 // Longest row the TREE family takes (128 slabs of 256 floats).
 constexpr int kTreeMaxCols = 128 * 256;
 

@@ -181,3 +181,22 @@ def test_run_without_device_reports_hip_error():
     assert lr.lr_softmax_f32(X, Y, 64, 12288, stream=0, workspace=WS, workspace_bytes=1 << 20) == lr.LR_ERR_HIP
     with pytest.raises(lr.LrError):
         lr.lr_workspace_query("layernorm", 64, 12289)
+
+
+def test_noalloc_refuses_an_oversized_plan_before_any_hip_call():
+    # 4096 rows x 64 segments x 8 B = 2 MiB of partials > the 1 MiB array
+    big = next(p for p in lr.lr_plan_enumerate(lr.lr_device_facts_mi355x(), "softmax", 4096, 1024,
+                                               "unordered_tree", 1)
+               if p.family == lr.LR_FAMILY_SPLIT and p.splits == 64)
+    assert lr.lr_plan_workspace_bytes(big, 4096) > (1 << 20)
+    assert lr.lr_run_f32_noalloc("softmax", 4096, 1024, 0.0, "unordered_tree", big, stream=0, x=X,
+                                 y=Y) == lr.LR_ERR_WORKSPACE
+    # the shared validation runs first, as in lr_run_f32
+    assert lr.lr_run_f32_noalloc("softmax", 4, 8, 0.0, 9, stream=0, x=X, y=Y) == lr.LR_ERR_INVALID_POLICY
+
+
+def test_noalloc_without_device_reports_hip_error():
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is present")
+    assert lr.lr_run_f32_noalloc("layernorm", 64, 12288, 1e-5, "unordered_tree", _split_plan(64, 12288),
+                                 stream=0, x=X, y=Y) == lr.LR_ERR_HIP
