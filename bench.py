@@ -66,6 +66,11 @@ SAMPLE_MS = 30.0
 SAMPLES = 9
 
 
+def progress(msg: str) -> None:
+    """A progress line on stderr (the JSON result alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def time_batches(torch, stream, launch, samples: int = SAMPLES, sample_ms: float = SAMPLE_MS,
                  warmup_ms: float = WARMUP_MS, calib: int = 200) -> dict:
     """Median, minimum and maximum microseconds per launch of `launch(i)`
@@ -146,6 +151,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the warm and cross-entropy context figures")
+    ap.add_argument("--samples", type=int, default=SAMPLES, help="per-op protocol: batches per op")
+    ap.add_argument("--sample-ms", type=float, default=SAMPLE_MS, help="per-op protocol: least duration of a batch")
+    ap.add_argument("--warmup-ms", type=float, default=WARMUP_MS, help="per-op protocol: least warm-up")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also launch a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -226,7 +234,12 @@ def main():
 
     # per-op launch duration: each op alone, the pages' protocol (warm-up of
     # at least 200 ms, nine batches of at least 30 ms, median and range)
-    per_op = {op: time_batches(torch, stream, lambda i, op=op: launch(op, i)) for op in OPS}
+    progress(f"timed {K} steps: {ms_per_step * 1e3:.2f} us per step")
+    per_op = {}
+    for op in OPS:
+        per_op[op] = time_batches(torch, stream, lambda i, op=op: launch(op, i), samples=args.samples,
+                                  sample_ms=args.sample_ms, warmup_ms=args.warmup_ms)
+        progress(f"{op}: {per_op[op]['median']:.3f} us per launch (median of {args.samples} batches)")
     per_op_us = {op: per_op[op]["median"] for op in OPS}
 
     b = op_bytes(ROWS, COLS)
@@ -283,9 +296,9 @@ def main():
         },
         "us_per_op": {op: round(per_op_us[op], 3) for op in OPS},
         "us_per_op_range": {op: [round(per_op[op]["min"], 3), round(per_op[op]["max"], 3)] for op in OPS},
-        "per_op_protocol": (f"median of {SAMPLES} batches of >= {SAMPLE_MS:.0f} ms of back-to-back cold launches "
-                            f"({per_op[OPS[0]]['launches_per_sample']} launches of {OPS[0]} per batch) after "
-                            f">= {WARMUP_MS:.0f} ms of warm-up, HIP events on the launch stream"),
+        "per_op_protocol": (f"median of {args.samples} batches of >= {args.sample_ms:g} ms of back-to-back cold "
+                            f"launches ({per_op[OPS[0]]['launches_per_sample']} launches of {OPS[0]} per batch) "
+                            f"after >= {args.warmup_ms:g} ms of warm-up, HIP events on the launch stream"),
         "single_call_us": single,
         "gbps_per_op": {op: round(gbps[op], 1) for op in OPS},
         "pct_of_hbm_peak_per_op": {op: round(100 * gbps[op] / HBM_PEAK_GBS, 2) for op in OPS},
@@ -322,8 +335,10 @@ def main():
             extra[f"{op}_768x6144_ordered_tree_cold"] = {"us_per_op": round(t["median"], 3),
                                                          "range": [round(t["min"], 3), round(t["max"], 3)],
                                                          "gbps": round(b / t["median"] / 1e3, 1)}
+        progress("warm-cache and ordered_tree figures done")
         extra.update(add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets))
         extra.update(small_configs_graph(lr, synth, torch, dev))
+        progress("fused residual LayerNorm and launch-bound workloads done")
         ce = synth.cross_entropy_inputs(4096, 32000, seed=0)
         cx = [torch.from_numpy(ce["logits"]).to(dev)]
         cx.append(cx[0].clone())
@@ -400,6 +415,7 @@ def main():
 
     # ---------------- CPU baseline: the oracle on the host cores ----------------
     if not args.no_cpu_baseline:
+        progress("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(soft, rms, ln, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)

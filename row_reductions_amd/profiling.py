@@ -107,6 +107,34 @@ def trace(trace_csv: str, kernels: list[str] | None = None) -> dict:
     return out
 
 
+def trace_runs(trace_csv: str, min_dispatches: int = 100) -> list[dict]:
+    """Consecutive runs of dispatches of one kernel instance with one grid
+    size, in trace order, with their count and average / median duration
+    (us): the phases of a script that times one shape after another.  Runs
+    shorter than `min_dispatches` (calibration, warm-up calls) are left out."""
+    import gzip
+    opener = gzip.open if trace_csv.endswith(".gz") else open
+    rows = []
+    with opener(trace_csv, "rt") as f:
+        for r in csv.DictReader(f):
+            grid = r.get("Grid_Size_X") or r.get("Grid_Size")
+            rows.append((int(r["Start_Timestamp"]), r["Kernel_Name"], int(grid),
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    runs, cur = [], None
+    for _, name, grid, d in rows:
+        if cur is None or (name, grid) != (cur["kernel"], cur["grid"]):
+            cur = {"kernel": name, "grid": grid, "durs": []}
+            runs.append(cur)
+        cur["durs"].append(d)
+    out = []
+    for r in runs:
+        d = sorted(r.pop("durs"))
+        if len(d) >= min_dispatches:
+            out.append(dict(r, dispatches=len(d), avg_us=sum(d) / len(d), median_us=d[len(d) // 2]))
+    return out
+
+
 def kernel_name(op_index: int, plan, aligned: bool, param_mode: int) -> str | None:
     """The demangled name of the kernel instance a CACHE or STREAM plan
     launches (param_mode: 0 no gamma/beta, 1 all present, 2 some)."""
@@ -147,8 +175,16 @@ def main(argv=None):
     tr.add_argument("--trace", required=True, help="rocprofv3 kernel-trace CSV")
     tr.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     tr.add_argument("--out", required=True)
+    ru = sub.add_parser("runs")
+    ru.add_argument("--trace", required=True, help="rocprofv3 kernel-trace CSV (or .csv.gz)")
+    ru.add_argument("--min-dispatches", type=int, default=100)
     sub.add_parser("hash")
     a = ap.parse_args(argv)
+    if a.cmd == "runs":
+        for r in trace_runs(a.trace, a.min_dispatches):
+            print(f"{r['dispatches']:7d} dispatches  grid {r['grid']:9d}  avg {r['avg_us']:8.3f} us  "
+                  f"median {r['median_us']:8.3f} us  {r['kernel']}")
+        return 0
     if a.cmd == "hash":
         print(csrc_hash())
         return 0

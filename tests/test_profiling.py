@@ -51,3 +51,22 @@ def test_committed_summary_covers_the_planned_kernels():
         assert r is not None, op
         # no re-reads: within 2% of the algorithmic 37,748,736 B
         assert abs(r["traffic_bytes"] / 37748736 - 1) < 0.02, (op, r["traffic_bytes"])
+
+
+TRACE = os.path.join(os.path.dirname(SUMMARY), "kernel_trace_768x6144.json")
+
+
+def test_committed_trace_covers_the_planned_kernels():
+    """The kernel-trace summary the bench's frac_trace reads names the very
+    instances the plans launch, with averages no shorter than a transfer of
+    the algorithmic bytes at 8 TB/s could take."""
+    with open(TRACE) as f:
+        s = json.load(f)
+    if s["csrc_sha256"] != profiling.csrc_hash():
+        pytest.skip("kernels changed since the trace was taken (the bench reports frac_trace: null)")
+    F = lr.lr_device_facts_mi355x()
+    for op, pm in (("softmax", 0), ("rmsnorm", 1), ("layernorm", 1)):
+        p = lr.lr_plan_for_device(F, op, 768, 6144, "unordered_tree", 1)
+        r = profiling.lookup(TRACE, op, profiling.kernel_name(lr.OPS[op], p, True, pm))
+        assert r is not None, op
+        assert r["avg_us"] > 37748736 / 8e12 * 1e6 and r["dispatches"] > 1000, (op, r)
