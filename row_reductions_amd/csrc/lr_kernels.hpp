@@ -187,6 +187,51 @@ __device__ __forceinline__ float4 param_load(const ParamRes& pr, bool present, i
     }
 }
 
+// The same chunk, on a misaligned row, read by a whole-wave team whose lanes
+// hold several chunks each.  For every chunk of a row but its first and its
+// last, p[4k - h] .. p[4k + 3 - h] lie inside p's blocks (they sit at grid
+// positions q .. q + 3, q = 4k + hp - h: q >= 4 - 3 > 0 for k >= 1, and
+// q + 4 <= cols + hp for every k below the last), so one 16-byte read at the
+// 4-byte aligned offset 4q returns the chunk.  `edge` (wave-uniform) says
+// this wave may hold the row's first or last chunk at this k: then the
+// two-block read above.  Being uniform, the test leaves the other waves'
+// reads straight-line.  On MI355X, against two reads for every chunk
+// (HIP-graph replays): LayerNorm 64 x 12289 5.88 -> 5.64 us, the fused
+// residual LayerNorm 64 x 12289 7.15 -> 6.61, RMSNorm 256 x 12289 6.55 ->
+// 6.26, RMSNorm 4096 x 1030 7.45 -> 7.03, LayerNorm 256 x 12289 7.56 -> 7.63.
+// (A per-lane test instead sent waves holding several rows down both paths:
+// LayerNorm 262144 x 50 24.8 -> 38.6 us.)  A chunk past the row reads zeros
+// or other elements of p, which are never used.  The two-block read is
+// written out here rather than shared with param_load: that is the form
+// measured above (the compiler schedules these kernels' store loops
+// differently otherwise).
+template <int PM>
+__device__ __forceinline__ float4 param_load_wide(const ParamRes& pr, bool present, int k, int h, float fill,
+                                                  bool edge) {
+    if constexpr (PM == kParNone) {
+        return splat4(fill);
+    } else {
+        float4 g;
+        if (!edge) {
+            g = res_ld4<kAuxDefault>(pr.r, (kVec * k + pr.hp - h) * 4);
+        } else {
+            const int d = pr.hp - h;
+            const int kb = k + (d >> 2);
+            const int sh = d & 3;
+            const float4 A = res_ld4<kAuxDefault>(pr.r, kb >= 0 ? kb * 16 : 0x7ffffff0);
+            const float4 B = res_ld4<kAuxDefault>(pr.r, kb * 16 + 16);
+            g.x = sh == 0 ? A.x : sh == 1 ? A.y : sh == 2 ? A.z : A.w;
+            g.y = sh == 0 ? A.y : sh == 1 ? A.z : sh == 2 ? A.w : B.x;
+            g.z = sh == 0 ? A.z : sh == 1 ? A.w : sh == 2 ? B.x : B.y;
+            g.w = sh == 0 ? A.w : sh == 1 ? B.x : sh == 2 ? B.y : B.z;
+        }
+        if constexpr (PM == kParRuntime) {
+            if (!present) g = splat4(fill);
+        }
+        return g;
+    }
+}
+
 // Parameters of a norm (gamma; gamma and beta for LayerNorm).
 template <int OP>
 constexpr int num_params() {
@@ -297,13 +342,29 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
             if constexpr (NP == 2) bpre[c] = param_load<AL, PM>(rb, a.beta != nullptr, chunk(c), h, cols, 0.0f);
         }
     }
+    // misaligned rows, whole-wave teams with several chunks per lane: does
+    // this wave's chunk c hold the row's first or last chunk (its lanes hold
+    // k = k0 .. k0 + 63)?  With one chunk per lane nearly every wave does:
+    // those plans keep the two-block read.
+    auto edge_of = [&](int c) {
+        const int k0 = t.s * kWave + W * c;
+        return k0 == 0 || (k0 < nv && nv <= k0 + kWave);
+    };
     auto gamma_of = [&](int c, int k) {
         if constexpr (NARROW && NP >= 1) return gpre[c];
-        return param_load<AL, PM>(rg, a.gamma != nullptr, k, h, cols, 1.0f);
+        if constexpr (!AL && NCH >= 2) {
+            return param_load_wide<PM>(rg, a.gamma != nullptr, k, h, 1.0f, edge_of(c));
+        } else {
+            return param_load<AL, PM>(rg, a.gamma != nullptr, k, h, cols, 1.0f);
+        }
     };
     auto beta_of = [&](int c, int k) {
         if constexpr (NARROW && NP == 2) return bpre[c];
-        return param_load<AL, PM>(rb, a.beta != nullptr, k, h, cols, 0.0f);
+        if constexpr (!AL && NCH >= 2) {
+            return param_load_wide<PM>(rb, a.beta != nullptr, k, h, 0.0f, edge_of(c));
+        } else {
+            return param_load<AL, PM>(rb, a.beta != nullptr, k, h, cols, 0.0f);
+        }
     };
 
     constexpr int AUX = LR_NT_LOADS ? kAuxNt : kAuxDefault;

@@ -232,8 +232,16 @@ __global__ void __launch_bounds__(1024) k_split_apply(const KArgs a) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int k = c.sb.k0 + t.w + W * i;
-        if constexpr (NP >= 1) gv[i] = param_load<AL, PM>(rg, a.gamma != nullptr, k, c.h, cols, 1.0f);
-        if constexpr (NP == 2) bv[i] = param_load<AL, PM>(rb, a.beta != nullptr, k, c.h, cols, 0.0f);
+        if constexpr (!AL && NCH >= 2) {
+            // does this wave (chunks k0 .. k0 + 63) hold the row's first or last chunk?
+            const int k0 = c.sb.k0 + t.s * kWave + W * i;
+            const bool edge = k0 == 0 || (k0 < c.nv && c.nv <= k0 + kWave);
+            if constexpr (NP >= 1) gv[i] = param_load_wide<PM>(rg, a.gamma != nullptr, k, c.h, 1.0f, edge);
+            if constexpr (NP == 2) bv[i] = param_load_wide<PM>(rb, a.beta != nullptr, k, c.h, 0.0f, edge);
+        } else {
+            if constexpr (NP >= 1) gv[i] = param_load<AL, PM>(rg, a.gamma != nullptr, k, c.h, cols, 1.0f);
+            if constexpr (NP == 2) bv[i] = param_load<AL, PM>(rb, a.beta != nullptr, k, c.h, cols, 0.0f);
+        }
     }
     const RowStats st = merge_partials<OP>(a, q, t.lane, c.nv, c.h);
     float* yr = a.y + c.row * (int64_t)cols;

@@ -4,8 +4,9 @@ parameters (whole-wave and sub-wave CACHE, STREAM, split rows through a
 workspace), each within |gpu - ref| <= 1e-6 + 1e-5 |ref| of the double
 oracle ("TIRx Metal reduction lowering", section 8, the affine step).
 Parameters off the grid make every call take the misaligned kernels, which
-read each parameter chunk as the two 16-byte blocks of the parameter's own
-grid that cover it."""
+read a parameter chunk as one 16-byte read at a 4-byte aligned offset, or
+(a row's first and last chunk, and rows packed several to a wave) as the two
+16-byte blocks of the parameter's own grid that cover it."""
 import numpy as np
 import pytest
 import torch
@@ -25,11 +26,14 @@ OFFSETS = [(0, 1, 2), (1, 3, 0), (2, 2, 2), (3, 0, 1)]  # (x and y, gamma, beta)
 
 def plans_for(op, rows, cols):
     """the first legal plan of each family for unaligned calls, plus a
-    sub-wave CACHE plan where there is one"""
+    sub-wave CACHE plan where there is one, and for whole-wave teams one with
+    several chunks per lane at one and at several waves per row (there only a
+    row's first and last chunk take the two-block read, in the waves that
+    hold them)"""
     facts = lr.lr_device_facts_query()
     out = {}
     for p in lr.lr_plan_enumerate(facts, op, rows, cols, "unordered_tree", 0):
-        key = (p.family, p.lanes_per_row < 64 * p.waves_per_row)
+        key = (p.family, p.lanes_per_row < 64 * p.waves_per_row, min(p.chunks_per_lane, 2), min(p.waves_per_row, 2))
         out.setdefault(key, p)
     return list(out.values())
 
