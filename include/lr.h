@@ -349,6 +349,28 @@ lr_status lr_run_f32(lr_op op, const lr_tensors* tensors, int64_t rows, int64_t 
                      lr_reduction_policy policy, const lr_plan* plan, void* workspace,
                      uint64_t workspace_bytes, hipStream_t stream);
 
+/* A measurement, not an operation of the pages: copies each row through the
+ * CACHE family's data path under `plan`,
+ *   y[r][j] = x[r][j],
+ * with the same workgroup per row, the same 16-byte buffer reads of the
+ * row's chunks (lane w of the team reads chunks w, w + W, ..., W = 64 x
+ * waves_per_row) and the same streamed stores as the reductions, with no
+ * arithmetic and no parameter read between them.  sync = 1: every wave
+ * waits for its reads and the workgroup meets at one barrier before the
+ * first store, as the reductions' cross-wave exchange makes them do; sync =
+ * 0: each wave stores as soon as its own reads land; any other value is
+ * LR_ERR_INVALID_ARGUMENT.  Its time under an operation's plan is the floor
+ * under that operation's launch-to-launch time ("Whole-launch reduction
+ * cost policy" measures whole launches).
+ * Aligned rows only: cols % 4 == 0 and x, y 16-byte aligned, else
+ * LR_ERR_MISALIGNED.  plan: a CACHE plan with rows_per_block 1, lanes_per_row
+ * 64 x waves_per_row, chunks_per_lane 1, 2, 3, 4, 6 or 8, whose lanes cover
+ * the row (64 x waves_per_row x chunks_per_lane x 4 >= cols), else
+ * LR_ERR_UNREALIZABLE_PLAN before any launch.  y may equal x; a partial
+ * overlap is LR_ERR_ALIASING.  rows == 0 returns LR_OK without a launch. */
+lr_status lr_copy_rows_f32(const float* x, float* y, int64_t rows, int64_t cols,
+                           const lr_plan* plan, int32_t sync, hipStream_t stream);
+
 /* Bytes of the device array lr_run_f32_noalloc uses in place of a workspace
  * (one copy per GPU, held until the process ends): room for 131072 split-row
  * partials, e.g. 2048 rows cut into 64 segments. */

@@ -120,6 +120,7 @@ def _load():
         "lr_add_layernorm_f32": [P, P, P, P, P, P, I64, I64, F32, I32, P],
         "lr_row_sum_f32": [P, P, I64, I64, I32, P],
         "lr_row_minmax_f32": [P, P, P, I64, I64, I32, P],
+        "lr_copy_rows_f32": [P, P, I64, I64, PP, I32, P],
         "lr_softmax_f32_with_plan": [P, P, I64, I64, I32, PP, P],
         "lr_rmsnorm_f32_with_plan": [P, P, P, I64, I64, F32, I32, PP, P],
         "lr_layernorm_f32_with_plan": [P, P, P, P, I64, I64, F32, I32, PP, P],
@@ -300,6 +301,11 @@ def lr_add_layernorm_f32(x, residual, gamma, beta, y, sum_out, rows, cols, eps, 
     return lib.lr_add_layernorm_f32_with_plan(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y),
                                               _ptr(sum_out), rows, cols, eps, _policy(policy),
                                               ctypes.byref(plan), _stream(stream))
+
+
+def lr_copy_rows_f32(x, y, rows, cols, plan, sync=1, stream=None) -> int:
+    """Row copy through the CACHE family's load/store path (a floor measurement)."""
+    return lib.lr_copy_rows_f32(_ptr(x), _ptr(y), rows, cols, ctypes.byref(plan), sync, _stream(stream))
 
 
 def lr_row_sum_f32(x, sums, rows, cols, policy=LR_UNORDERED_TREE, stream=None, plan=None, workspace=None,

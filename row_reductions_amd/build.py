@@ -49,6 +49,7 @@ SOURCES = [
     "k_add_layernorm.hip",
     "k_row_sum.hip",
     "k_row_minmax.hip",
+    "k_copy_rows.hip",
     "k_ordered.hip",
     "k_ordered_lane.hip",
     *[f"k_tree_{op}.hip" for op in TREE_OPS],

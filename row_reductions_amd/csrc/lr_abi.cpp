@@ -341,6 +341,24 @@ lr_status lr_row_minmax_f32(const float* x, float* mins, float* maxs, int64_t ro
 
 static lr_status need_plan(const lr_plan* plan) { return plan == nullptr ? LR_ERR_NULL_POINTER : LR_OK; }
 
+lr_status lr_copy_rows_f32(const float* x, float* y, int64_t rows, int64_t cols, const lr_plan* plan,
+                           int32_t sync, hipStream_t stream) {
+    if (plan == nullptr) return LR_ERR_NULL_POINTER;
+    if (sync != 0 && sync != 1) return LR_ERR_INVALID_ARGUMENT;
+    if (rows < 0 || cols <= 0 || rows > INT32_MAX || cols > INT32_MAX / 4) return LR_ERR_INVALID_SHAPE;
+    if (rows == 0) return LR_OK;
+    if (x == nullptr || y == nullptr) return LR_ERR_NULL_POINTER;
+    if (cols % 4 != 0 || !lr::aligned16(x) || !lr::aligned16(y)) return LR_ERR_MISALIGNED;
+    const int64_t tb = rows * cols * 4;
+    if (x != y && lr::overlap(lr::range_of(x, tb), lr::range_of(y, tb))) return LR_ERR_ALIASING;
+    const int S = plan->waves_per_row, n = plan->chunks_per_lane;
+    const bool compiled = n == 1 || n == 2 || n == 3 || n == 4 || n == 6 || n == 8;
+    if (plan->family != LR_FAMILY_CACHE || plan->rows_per_block != 1 || S < 1 || S > 16 ||
+        plan->lanes_per_row != 64 * S || !compiled || (int64_t)64 * S * n * 4 < cols)
+        return LR_ERR_UNREALIZABLE_PLAN;
+    return lr::launch_copy_rows(x, y, rows, (int)cols, *plan, sync == 1, stream) == hipSuccess ? LR_OK : LR_ERR_HIP;
+}
+
 lr_status lr_softmax_f32_with_plan(const float* x, float* y, int64_t rows, int64_t cols,
                                    lr_reduction_policy policy, const lr_plan* plan, hipStream_t stream) {
     if (need_plan(plan) != LR_OK) return LR_ERR_NULL_POINTER;

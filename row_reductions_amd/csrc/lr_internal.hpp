@@ -81,6 +81,9 @@ hipError_t launch_cross_entropy(const KArgs& a, const lr_plan& p, bool aligned, 
 hipError_t launch_add_layernorm(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_row_sum(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
 hipError_t launch_row_minmax(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t s);
+// Row copy through the CACHE family's load/store path (k_copy_rows.hip).
+hipError_t launch_copy_rows(const float* x, float* y, int64_t rows, int cols, const lr_plan& p, bool sync,
+                            hipStream_t s);
 hipError_t launch_ordered(int op, int policy, const KArgs& a, const lr_plan& p, hipStream_t s);
 // The ordered policies with one lane per row (lanes_per_row = 1: narrow
 // rows, one wavefront of 64 rows per workgroup).

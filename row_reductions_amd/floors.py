@@ -21,6 +21,16 @@ Every point is timed as HIP-graph replays (200 launches per graph, resident
 inputs), median of five batches of >= 30 ms after >= 200 ms of warm-up, as
 the bench times its launch-bound workloads.
 
+The copy floor at 768 x 6144, cold: under the plan each of softmax, RMSNorm
+and LayerNorm launches with, the row copy (lr_copy_rows_f32: the same
+workgroups, reads and stores, no arithmetic between them), each wave storing
+as soon as its reads land, and with the reads of the whole workgroup landed
+and one barrier before the first store (the reductions' shape), beside the
+operation itself.  The copy's time is what moving the bytes through that
+launch shape costs; the difference is the operation's own work.  Then the
+copy, both ways, under every one-row CACHE plan it compiles: its fastest is
+the floor of a launch of this size.
+
 RMSNorm and LayerNorm, 768 x 6144, with and without their per-column
 parameters (gamma; gamma and beta), each at the plan the library picks and
 at six waves per row, cold (32 rotating buffer sets, as the bench): the
@@ -202,6 +212,47 @@ def main(argv=None):
                 par[key] = round(_time_cold(fn, sets), 3)
                 print(f"{key}: {par[key]} us", flush=True)
     out["params_768x6144_cold_us"] = par
+    # the copy floor: each operation's own plan with the row copy (the same
+    # reads and stores, nothing between them) in place of the operation
+    cp = {}
+    for op in ("softmax", "rmsnorm", "layernorm"):
+        plan = lr.lr_plan_query(op, rows, cols, "unordered_tree")
+        pp = ctypes.byref(plan)
+        if op == "softmax":
+            fn = lambda k, pp=pp: lr.lib.lr_softmax_f32_with_plan(xp[k], yp[k], rows, cols, 0, pp, sh)
+        elif op == "rmsnorm":
+            fn = lambda k, pp=pp: lr.lib.lr_rmsnorm_f32_with_plan(xp[k], gp, yp[k], rows, cols, 1e-6, 0, pp, sh)
+        else:
+            fn = lambda k, pp=pp: lr.lib.lr_layernorm_f32_with_plan(xp[k], gp, bp, yp[k], rows, cols, 1e-5, 0, pp, sh)
+        copy = lambda k, pp=pp: lr.lib.lr_copy_rows_f32(xp[k], yp[k], rows, cols, pp, 0, sh)
+        copy_sync = lambda k, pp=pp: lr.lib.lr_copy_rows_f32(xp[k], yp[k], rows, cols, pp, 1, sh)
+        rec = {"plan": f"S={plan.waves_per_row}, {plan.chunks_per_lane} chunks"}
+        for _ in range(2):  # each config twice, interleaved: the lower median of the two
+            for key, f in (("op_us", fn), ("copy_us", copy), ("copy_sync_us", copy_sync)):
+                t = _time_cold(f, sets)
+                rec[key] = round(min(rec.get(key, t), t), 3)
+        rec["gap_to_copy_sync_us"] = round(rec["op_us"] - rec["copy_sync_us"], 3)
+        for key in ("op_us", "copy_us", "copy_sync_us"):
+            rec[key.replace("_us", "_frac_of_8TBps")] = round(2 * rows * cols * 4 / (rec[key] * 1e-6) / 8e12, 4)
+        cp[op] = rec
+        print(f"copy floor {op}: {rec}", flush=True)
+    out["copy_768x6144_cold_us"] = cp
+    # the same copy under every one-row CACHE plan the copy compiles: the
+    # fastest a launch of this shape moves these bytes
+    sweep = {}
+    for p in lr.lr_plan_enumerate(facts, "softmax", rows, cols, "unordered_tree", 1):
+        if (p.family != lr.LR_FAMILY_CACHE or p.rows_per_block != 1 or p.lanes_per_row != 64 * p.waves_per_row
+                or p.chunks_per_lane not in (1, 2, 3, 4, 6, 8)):
+            continue
+        pp = ctypes.byref(p)
+        key = f"S={p.waves_per_row}, {p.chunks_per_lane} chunks"
+        sweep[key] = {f"sync{sy}": round(_time_cold(lambda k, pp=pp, sy=sy: lr.lib.lr_copy_rows_f32(
+            xp[k], yp[k], rows, cols, pp, sy, sh), sets), 3) for sy in (0, 1)}
+        print(f"copy sweep {key}: {sweep[key]}", flush=True)
+    best = min(((v, k, m) for k, r in sweep.items() for m, v in r.items()))
+    out["copy_sweep_768x6144_cold_us"] = {"plans": sweep, "best_us": best[0], "best_plan": best[1],
+                                          "best_mode": best[2],
+                                          "best_frac_of_8TBps": round(2 * rows * cols * 4 / (best[0] * 1e-6) / 8e12, 4)}
     del xs, ys
     out["tiny_softmax_1x64_us"] = round(out["tiny_softmax_1x64_us"], 3)
     print(json.dumps(out) if args.json else json.dumps(out, indent=1), flush=True)

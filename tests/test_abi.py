@@ -200,3 +200,30 @@ def test_noalloc_without_device_reports_hip_error():
         pytest.skip("a GPU is present")
     assert lr.lr_run_f32_noalloc("layernorm", 64, 12288, 1e-5, "unordered_tree", _split_plan(64, 12288),
                                  stream=0, x=X, y=Y) == lr.LR_ERR_HIP
+
+
+def test_copy_rows_validates_before_any_hip_call():
+    F = lr.lr_device_facts_mi355x()
+    p = lr.lr_plan_for_device(F, "rmsnorm", 768, 6144, "unordered_tree", 1)
+    assert p.family == lr.LR_FAMILY_CACHE and p.rows_per_block == 1
+    assert lr.lr_copy_rows_f32(X, Y, 0, 6144, p, 1, 0) == lr.LR_OK  # nothing to launch
+    assert lr.lib.lr_copy_rows_f32(X, Y, 4, 6144, None, 1, 0) == lr.LR_ERR_NULL_POINTER
+    assert lr.lr_copy_rows_f32(X, Y, 4, 6144, p, 2, 0) == lr.LR_ERR_INVALID_ARGUMENT
+    assert lr.lr_copy_rows_f32(None, Y, 4, 6144, p, 1, 0) == lr.LR_ERR_NULL_POINTER
+    assert lr.lr_copy_rows_f32(X, Y, -1, 6144, p, 1, 0) == lr.LR_ERR_INVALID_SHAPE
+    assert lr.lr_copy_rows_f32(X, Y, 4, 6142, p, 1, 0) == lr.LR_ERR_MISALIGNED
+    assert lr.lr_copy_rows_f32(X + 4, Y, 4, 6144, p, 1, 0) == lr.LR_ERR_MISALIGNED
+    assert lr.lr_copy_rows_f32(X, X + 16, 4, 6144, p, 1, 0) == lr.LR_ERR_ALIASING
+    # lanes that do not cover the row
+    assert lr.lr_copy_rows_f32(X, Y, 4, 64 * p.waves_per_row * p.chunks_per_lane * 4 + 4, p, 1, 0) \
+        == lr.LR_ERR_UNREALIZABLE_PLAN
+    # not a one-row CACHE plan, or a chunk count with no compiled copy
+    st = next(q for q in lr.lr_plan_enumerate(F, "rmsnorm", 768, 6144, "unordered_tree", 1)
+              if q.family == lr.LR_FAMILY_STREAM)
+    assert lr.lr_copy_rows_f32(X, Y, 4, 6144, st, 1, 0) == lr.LR_ERR_UNREALIZABLE_PLAN
+    packed = next(q for q in lr.lr_plan_enumerate(F, "softmax", 768, 256, "unordered_tree", 1)
+                  if q.family == lr.LR_FAMILY_CACHE and q.rows_per_block > 1)
+    assert lr.lr_copy_rows_f32(X, Y, 4, 256, packed, 1, 0) == lr.LR_ERR_UNREALIZABLE_PLAN
+    big = next(q for q in lr.lr_plan_enumerate(F, "softmax", 4, 32768, "unordered_tree", 1)
+               if q.family == lr.LR_FAMILY_CACHE and q.chunks_per_lane == 16)
+    assert lr.lr_copy_rows_f32(X, Y, 4, 32768, big, 1, 0) == lr.LR_ERR_UNREALIZABLE_PLAN
