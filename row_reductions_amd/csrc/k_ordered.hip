@@ -265,12 +265,26 @@ __global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
             }
         } else {
             const BufRes ry = make_res(a.y + row * (int64_t)cols, cols * 4);
+            const float y = 1.0f / s;
             for (int base = 0; base < cols; base += kWave * kPass) {
                 float v[kPass];
 #pragma unroll
                 for (int u = 0; u < kPass; ++u) v[u] = res_ld1(rx, pass_elem(base, u, lane) * 4);
+                // e / s rounded once: div_rowsum unless some e of the trip
+                // lies in (0, 2^-96), then the division (a choice per wave)
+                unsigned lo = ~0u;
 #pragma unroll
-                for (int u = 0; u < kPass; ++u) res_st1(ry, pass_elem(base, u, lane) * 4, expf(v[u] - m) / s);
+                for (int u = 0; u < kPass; ++u) {
+                    v[u] = expf(v[u] - m);
+                    lo = min(lo, rowsum_guard(v[u]));
+                }
+                if (__builtin_amdgcn_ballot_w64(lo < kRowsumTiny) == 0) {
+#pragma unroll
+                    for (int u = 0; u < kPass; ++u) res_st1(ry, pass_elem(base, u, lane) * 4, div_rowsum(v[u], s, y));
+                } else {
+#pragma unroll
+                    for (int u = 0; u < kPass; ++u) res_st1(ry, pass_elem(base, u, lane) * 4, v[u] / s);
+                }
             }
         }
     } else if constexpr (OP == kRowSum) {

@@ -202,9 +202,19 @@ __device__ __forceinline__ void lane_body(const KArgs& a, float* tile) {
                 a.losses[row] = logf(s) + (m - sel);
             }
         } else {
+            // e / s rounded once: div_rowsum unless some e of the wave's rows
+            // lies in (0, 2^-96), then the division (a choice per wave)
+            const float y = 1.0f / s;
+            unsigned lo = ~0u;
 #pragma unroll
-            for (int j = 0; j < N; ++j)
-                tile[lane * pitch + min(j, cols)] = e[j] / s;
+            for (int j = 0; j < N; ++j) lo = min(lo, rowsum_guard(e[j]));
+            if (__builtin_amdgcn_ballot_w64(lo < kRowsumTiny) == 0) {
+#pragma unroll
+                for (int j = 0; j < N; ++j) tile[lane * pitch + min(j, cols)] = div_rowsum(e[j], s, y);
+            } else {
+#pragma unroll
+                for (int j = 0; j < N; ++j) tile[lane * pitch + min(j, cols)] = e[j] / s;
+            }
             wave_sync();
             copy_out(a.y);
         }

@@ -233,6 +233,27 @@ __device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_log
 
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// a / s rounded once (the IEEE quotient) in three instructions, for s >= 1
+// and y = 1 / s rounded once: q = a y, r = a - s q (exact, by the fused
+// multiply-add), then q + r y rounded once (P. Markstein's correction of a
+// quotient from a correctly rounded reciprocal, IBM J. Res. Dev. 34(1),
+// 1990).  The argument needs q and r clear of the subnormal range; a == 0
+// or a >= 2^-96 keeps them there (q >= 2^-120).  Below that the result can
+// be one unit off (a near 2^-121 and smaller), so callers check their
+// numerators with rowsum_guard first.  The translation units that call this
+// must not contract a * y into the fma.
+__device__ __forceinline__ float div_rowsum(float a, float s, float y) {
+    const float q = a * y;
+    return __builtin_fmaf(__builtin_fmaf(-q, s, a), y, q);
+}
+
+// The unsigned minimum of rowsum_guard(a) over a set of non-negative
+// numerators is below kRowsumTiny exactly when one of them lies in
+// (0, 2^-96), where div_rowsum may differ from the division: the bit pattern
+// minus one, so that zeros wrap to the top.
+constexpr unsigned kRowsumTiny = 0x0F7FFFFFu;  // bits(2^-96) - 1
+__device__ __forceinline__ unsigned rowsum_guard(float a) { return __float_as_uint(a) - 1u; }
+
 __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
 // Softmax state over a row team with one exchange: every wave brings its

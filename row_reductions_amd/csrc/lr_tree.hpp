@@ -140,12 +140,32 @@ __device__ __forceinline__ void tree_body(const KArgs& a, float (&red)[2][kMaxWa
                 a.losses[row] = logf(s) + (m - sel);
             }
         } else {
+            // e / s rounded once: div_rowsum unless some e of this wave lies
+            // in (0, 2^-96), then the division (a choice per wave)
+            unsigned lo = ~0u;
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int k = chunk(c);
-                if (k < nv) {
-                    const float4 o = make_float4(v[c].x / s, v[c].y / s, v[c].z / s, v[c].w / s);
-                    store_chunk<AL>(yr, a.y_same_phase, k, 0, cols, o);
+            for (int c = 0; c < NCH; ++c)
+                lo = min(min(min(lo, rowsum_guard(v[c].x)), rowsum_guard(v[c].y)),
+                         min(rowsum_guard(v[c].z), rowsum_guard(v[c].w)));
+            if (__builtin_amdgcn_ballot_w64(lo < kRowsumTiny) == 0) {
+                const float y = 1.0f / s;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const int k = chunk(c);
+                    if (k < nv) {
+                        const float4 o = make_float4(div_rowsum(v[c].x, s, y), div_rowsum(v[c].y, s, y),
+                                                     div_rowsum(v[c].z, s, y), div_rowsum(v[c].w, s, y));
+                        store_chunk<AL>(yr, a.y_same_phase, k, 0, cols, o);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const int k = chunk(c);
+                    if (k < nv) {
+                        const float4 o = make_float4(v[c].x / s, v[c].y / s, v[c].z / s, v[c].w / s);
+                        store_chunk<AL>(yr, a.y_same_phase, k, 0, cols, o);
+                    }
                 }
             }
         }

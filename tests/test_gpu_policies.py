@@ -165,3 +165,41 @@ def test_ordered_tree_repeatable():
     first = run("softmax", inp, "ordered_tree")
     for _ in range(10):
         assert np.array_equal(run("softmax", inp, "ordered_tree").view(np.uint32), first.view(np.uint32))
+
+
+def test_ordered_tree_softmax_tiny_exponentials():
+    """Outputs e / s are rounded once under every plan.  TREE plans compute
+    them as q = e y, then q + (e - s q) y rounded once, y = 1 / s, and switch
+    a wave to the division when one of its e lies in (0, 2^-96), where that
+    form can be one unit off; ORDERED plans divide.  Rows here put x - max
+    down to -104, so e runs through 2^-96 and the subnormals: whole rows of
+    waves on the division, rows with one such e (one wave switches, the rest
+    do not), and rows with none.  Every plan must give the same bits."""
+    facts = lr.lr_device_facts_query()
+    for rows, cols in [(9, 6144), (6, 1000), (4, 12288)]:
+        rng = np.random.default_rng(rows * cols)
+        x = np.empty((rows, cols), dtype=np.float32)
+        for r in range(rows):
+            kind = r % 3
+            if kind == 0:    # spread to -104: most waves meet e < 2^-96
+                x[r] = (-104.0 * rng.random(cols)).astype(np.float32)
+            elif kind == 1:  # one element at -80 in an ordinary row
+                x[r] = (-8.0 * rng.random(cols)).astype(np.float32)
+                x[r, rng.integers(cols)] = -80.0
+            else:            # none below 2^-96
+                x[r] = (-30.0 * rng.random(cols)).astype(np.float32)
+            x[r, rng.integers(cols)] = 0.0
+        inp = {"x": x}
+        plans = lr.lr_plan_enumerate(facts, "softmax", rows, cols, "ordered_tree", 1 if cols % 4 == 0 else 0)
+        fams = sorted({p.family for p in plans})
+        assert lr.LR_FAMILY_TREE in fams and lr.LR_FAMILY_ORDERED in fams, fams
+        print(f"\n[gpu] softmax tiny exponentials {rows}x{cols}: {len(plans)} plans", flush=True)
+        first = None
+        for p in plans:
+            got = run("softmax", inp, "ordered_tree", plan=p)
+            check("softmax", inp, "ordered_tree", got, f"tiny exponentials {rows}x{cols} {p}")
+            if first is None:
+                first = got
+            assert np.array_equal(got.view(np.uint32), first.view(np.uint32)), p
+        sub = (first > 0) & (first < np.float32(2.0 ** -96))
+        assert sub.any()  # the slow path's outputs are really there
