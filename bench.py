@@ -329,13 +329,15 @@ def main():
                 extra[f"{op}_768x6144_warm"] = {"us_per_op": round(t["median"], 3),
                                                 "range": [round(t["min"], 3), round(t["max"], 3)],
                                                 "gbps": round(b / t["median"] / 1e3, 1)}
-        # the deterministic ordered_tree policy on the same step (cold)
-        for op in OPS:
-            t = time_batches(torch, stream, lambda i, op=op: launch(op, i, lr.LR_ORDERED_TREE), samples=5)
-            extra[f"{op}_768x6144_ordered_tree_cold"] = {"us_per_op": round(t["median"], 3),
-                                                         "range": [round(t["min"], 3), round(t["max"], 3)],
-                                                         "gbps": round(b / t["median"] / 1e3, 1)}
-        progress("warm-cache and ordered_tree figures done")
+        # the deterministic policies on the same step (cold)
+        for pol, pname in ((lr.LR_ORDERED_TREE, "ordered_tree"), (lr.LR_ORDERED_FOLD, "ordered_fold"),
+                           (lr.LR_FOLD_RIGHT, "fold_right")):
+            for op in OPS:
+                t = time_batches(torch, stream, lambda i, op=op, pol=pol: launch(op, i, pol), samples=5)
+                extra[f"{op}_768x6144_{pname}_cold"] = {"us_per_op": round(t["median"], 3),
+                                                        "range": [round(t["min"], 3), round(t["max"], 3)],
+                                                        "gbps": round(b / t["median"] / 1e3, 1)}
+        progress("warm-cache and ordered-policy figures done")
         extra.update(add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets))
         extra.update(small_configs_graph(lr, synth, torch, dev))
         progress("fused residual LayerNorm and launch-bound workloads done")
