@@ -89,3 +89,30 @@ def test_masked_rows_every_plan(op):
                     assert (got[masked].view(np.uint32) == 0).all(), what  # +0 exactly
                 n += 1
     assert n > 100
+
+
+def test_ordered_softmax_of_tied_maxima_is_exact():
+    """A row holding k copies of its maximum and -inf elsewhere has
+    numerators exactly 1 and 0 (exp(0) = 1, exp(-inf) = 0) and sum exactly k
+    (k < 2^24), so under an ordered policy, whose outputs are the quotient
+    rounded once, each output is exactly fl(1/k) or +0: bit for bit, under
+    every plan, whatever the device's exp does elsewhere."""
+    facts = lr.lr_device_facts_query()
+    for rows, cols in [(7, 4096), (5, 1030), (9, 64), (3, 20000)]:
+        rng = np.random.default_rng(cols)
+        x = np.full((rows, cols), -np.inf, dtype=np.float32)
+        ks = []
+        for r in range(rows):
+            k = int(rng.integers(1, cols + 1)) if r % 2 else [1, 3, 7, 41, cols][r // 2 % 5]
+            k = min(k, cols)
+            x[r, rng.choice(cols, size=k, replace=False)] = 2.5
+            ks.append(k)
+        want = np.where(np.isneginf(x), np.float32(0.0),
+                        (np.float32(1.0) / np.array(ks, dtype=np.float32))[:, None]).astype(np.float32)
+        for policy in ["ordered_fold", "ordered_tree", "fold_right"]:
+            plans = lr.lr_plan_enumerate(facts, "softmax", rows, cols, policy, 1 if cols % 4 == 0 else 0)
+            print(f"\n[gpu] tied maxima {rows}x{cols} {policy}: {len(plans)} plans", flush=True)
+            for p in plans + [None]:
+                got, st, _ = run_gpu("softmax", {"x": x}, None, policy, plan=p)
+                assert st == lr.LR_OK, (p, lr.lr_status_string(st))
+                assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (rows, cols, policy, p)
