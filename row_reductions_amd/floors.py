@@ -122,10 +122,46 @@ def _fit(xs, ts):
     return float(a), float(b)
 
 
+def counter_launches(n: int) -> int:
+    """Softmax, and RMSNorm and LayerNorm with and without their parameters,
+    768 x 6144 at the library's plans, n cold launches each (32 rotating
+    buffer sets) and no timing: the program to run under a counter pass,
+    whose per-kernel figures then belong to one launch configuration each."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(0)
+    rows, cols, sets = 768, 6144, 32
+    xs = [torch.randn(rows, cols, device=dev, generator=g) for _ in range(sets)]
+    ys = [torch.empty_like(t) for t in xs]
+    gm = torch.rand(cols, device=dev, generator=g) + 0.5
+    bt = torch.randn(cols, device=dev, generator=g) * 0.1
+    sh = torch.cuda.current_stream().cuda_stream
+    xp, yp = [t.data_ptr() for t in xs], [t.data_ptr() for t in ys]
+    gp, bp = gm.data_ptr(), bt.data_ptr()
+    calls = [
+        ("softmax", lambda k: lr.lib.lr_softmax_f32(xp[k], yp[k], rows, cols, 0, sh)),
+        ("rmsnorm with gamma", lambda k: lr.lib.lr_rmsnorm_f32(xp[k], gp, yp[k], rows, cols, 1e-6, 0, sh)),
+        ("rmsnorm without", lambda k: lr.lib.lr_rmsnorm_f32(xp[k], None, yp[k], rows, cols, 1e-6, 0, sh)),
+        ("layernorm with gamma, beta", lambda k: lr.lib.lr_layernorm_f32(xp[k], gp, bp, yp[k], rows, cols, 1e-5, 0, sh)),
+        ("layernorm without", lambda k: lr.lib.lr_layernorm_f32(xp[k], None, None, yp[k], rows, cols, 1e-5, 0, sh)),
+    ]
+    for name, fn in calls:
+        for i in range(n):
+            lr.check(fn(i % sets), name)
+        torch.cuda.synchronize()
+        print(f"{name}: {n} launches", flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--json", action="store_true")
+    ap.add_argument("--counter-launches", type=int, default=0, metavar="N",
+                    help="only launch the 768x6144 norms with and without parameters (and softmax) N times "
+                         "each, untimed: the program for a counter pass")
     args = ap.parse_args(argv)
+    if args.counter_launches:
+        return counter_launches(args.counter_launches)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     g = torch.Generator(device=dev).manual_seed(0)

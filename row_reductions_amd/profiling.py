@@ -51,6 +51,21 @@ def _per_kernel(path: str):
     return vals, order
 
 
+def counter_means(path: str) -> dict:
+    """Per kernel, the mean over its dispatches of every counter in a
+    rocprofv3 counter-collection CSV (one row per dispatch and counter)."""
+    acc = defaultdict(lambda: defaultdict(list))
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = {}
+    for name, per in acc.items():
+        rec = {c: sum(v) / len(v) for c, v in per.items()}
+        rec["dispatches"] = max(len(v) for v in per.values())
+        out[name] = rec
+    return out
+
+
 def kernel_op(name: str):
     m = re.search(r"lr::k_(cache|stream|ordered)<(\d+)", name)
     return OP_NAMES.get(int(m.group(2))) if m else None
@@ -179,7 +194,14 @@ def main(argv=None):
     ru.add_argument("--trace", required=True, help="rocprofv3 kernel-trace CSV (or .csv.gz)")
     ru.add_argument("--min-dispatches", type=int, default=100)
     sub.add_parser("hash")
+    co = sub.add_parser("counters")
+    co.add_argument("--csv", required=True, help="rocprofv3 counter-collection CSV")
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        for name, rec in counter_means(a.csv).items():
+            vals = "  ".join(f"{c} {v:.6g}" for c, v in sorted(rec.items()) if c != "dispatches")
+            print(f"{rec['dispatches']:6d} dispatches  {vals}  {name}")
+        return 0
     if a.cmd == "runs":
         for r in trace_runs(a.trace, a.min_dispatches):
             print(f"{r['dispatches']:7d} dispatches  grid {r['grid']:9d}  avg {r['avg_us']:8.3f} us  "
