@@ -163,7 +163,8 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the row-reduction path has no multi-GPU part "
-              "(rows are independent; sharding is described in DESIGN.md).", file=sys.stderr)
+              "(rows are independent: G GPUs would each run the same kernels on rows / G rows, "
+              "with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
