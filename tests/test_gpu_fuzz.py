@@ -2,12 +2,15 @@
 reduction policy, a ragged shape (cols log-uniform in 1 .. 20000), a plan
 (the automatic one, or any legal plan of lr_plan_enumerate, split-row plans
 with a workspace of their own), 4-byte offsets of the input and output rows
-from their 16-byte grid, an in-place call, optional gamma / beta and, for
+from their 16-byte grid, an in-place call, optional gamma / beta (each at a
+4-byte offset of its own from the grid) and, for
 cross-entropy, labels out of range.  Every output sits between guard regions
 that must survive.  Gates ("TIRx Metal reduction lowering", section 1, the
 reduction policies):
   unordered_tree  |gpu - ref| <= 1e-6 + 1e-5 |ref| against the double oracle
-                  (row sums: 1e-6 + 1e-5 sum |x|);
+                  (row sums: 1e-6 + 1e-5 sum |x|; LayerNorm rows whose mean
+                  exceeds 8 standard deviations add the FP32 rounding of
+                  the mean, layernorm_bar);
   ordered ones    RMSNorm, LayerNorm, the fused residual LayerNorm and row
                   sums equal the CPU FP32 replay of the policy bit for bit;
                   softmax and cross-entropy (the device's exp/log) lie within
@@ -30,7 +33,7 @@ pytestmark = pytest.mark.gpu
 OPS = ["softmax", "rmsnorm", "layernorm", "cross_entropy", "add_layernorm", "row_sum", "row_minmax"]
 POLICIES = ["unordered_tree", "ordered_fold", "ordered_tree", "fold_right"]
 EPS = {"rmsnorm": 1e-6, "layernorm": 1e-5, "add_layernorm": 1e-5}
-CASES = 160
+CASES = 640
 
 
 def draw(k):
@@ -48,8 +51,10 @@ def draw(k):
     has_g = g.random() < 0.7
     has_b = g.random() < 0.7
     with_sum = op == "add_layernorm" and g.random() < 0.5
+    go = int(g.integers(0, 4))  # drawn last: the earlier draws keep their values
+    bo = int(g.integers(0, 4))
     return dict(op=op, policy=policy, rows=rows, cols=cols, xo=xo, yo=0 if in_place else yo, in_place=in_place,
-                use_plan=use_plan, pick=pick, has_g=has_g, has_b=has_b, with_sum=with_sum, seed=k)
+                use_plan=use_plan, pick=pick, has_g=has_g, has_b=has_b, with_sum=with_sum, go=go, bo=bo, seed=k)
 
 
 def inputs(c):
@@ -87,6 +92,38 @@ def choose_plan(c, aligned):
     return plans[min(len(plans) - 1, int(c["pick"] * len(plans)))]
 
 
+def layernorm_bar(x, gam, eps, ref):
+    """The parity bar of an unordered LayerNorm, per element.  Rows whose
+    mean lies within 8 of their standard deviations of zero keep the stated
+    bar 1e-6 + 1e-5 |ref|.  On other rows (a large mean over a small spread:
+    two nearly equal values, say) the FP32 two-pass method ("TIRx Metal
+    reduction lowering", section 5.1) carries the rounding of the mean into
+    every centred value, whatever the kernel: an FP32 sum of n values in any
+    order of depth at most D = ceil(n / 64) + 14 (a lane's serial run, then
+    trees over lanes and waves) is off by at most D u sum|x|, so the mean by
+    D u mean|x|, and each output by that times r |gamma|, r = 1 / sqrt(var +
+    eps); those rows get that term on top."""
+    xd = x.astype(np.float64)
+    n = x.shape[1]
+    mu = xd.mean(axis=1, keepdims=True)
+    var = ((xd - mu) ** 2).mean(axis=1, keepdims=True)
+    bar = ATOL + RTOL * np.abs(ref)
+    ill = np.abs(mu) > 8.0 * np.sqrt(var)
+    depth = math.ceil(n / 64) + 14
+    term = depth * 2.0 ** -24 * np.abs(xd).mean(axis=1, keepdims=True) / np.sqrt(var + eps)
+    term = term * (np.abs(gam.astype(np.float64)) if gam is not None else 1.0)
+    return bar + np.where(ill, term, 0.0)
+
+
+def assert_layernorm(got, ref, x, gam, eps, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    bound = layernorm_bar(x, gam, eps, ref)
+    if not (err <= bound).all():
+        i = np.unravel_index(np.argmax(err / bound), ref.shape)
+        raise AssertionError(f"{what}: parity fails at {i}: gpu={got[i]!r} ref={ref[i]!r} "
+                             f"(worst err/bound {(err / bound).max():.3g})")
+
+
 def ordered_bound(op, policy, n):
     steps = max(1, math.ceil(math.log2(n))) if policy == "ordered_tree" else max(1, n - 1)
     return steps * 2.0 ** -24 / (1 - steps * 2.0 ** -24)
@@ -104,10 +141,13 @@ def test_random_case(k):
     if plan is not None and plan.family == lr.LR_FAMILY_SPLIT:
         ws = torch.full((lr.lr_plan_workspace_bytes(plan, rows),), 0xFF, dtype=torch.uint8, device=DEV)
     print(f"\n[gpu] fuzz {k}: {op} {rows}x{cols} {policy} xo={c['xo']} yo={c['yo']} in_place={c['in_place']} "
-          f"gamma={'gamma' in d} beta={'beta' in d} sum={c['with_sum']} plan={plan}", flush=True)
+          f"gamma={'gamma' in d}+{c['go']} beta={'beta' in d}+{c['bo']} sum={c['with_sum']} plan={plan}", flush=True)
     xv, xfull = placed(x, c["xo"])
-    dv = {n: (torch.from_numpy(np.ascontiguousarray(d[n])).to(DEV) if n in d else None)
-          for n in ("gamma", "beta", "labels")}
+    dv = {"labels": torch.from_numpy(np.ascontiguousarray(d["labels"])).to(DEV) if "labels" in d else None}
+    params = {}  # gamma / beta at their drawn 4-byte offsets, between guards that must survive
+    for n, off in (("gamma", c["go"]), ("beta", c["bo"])):
+        params[n] = placed(d[n], off) if n in d else (None, None)
+        dv[n] = params[n][0]
     outs = []  # (view, full buffer) of each output, guards checked below
     if op in ("cross_entropy", "row_sum", "row_minmax"):
         o1 = placed(np.zeros(rows, np.float32), c["yo"])
@@ -146,6 +186,10 @@ def test_random_case(k):
     assert st == lr.LR_OK, lr.lr_status_string(st)
     for view, full in outs:
         assert guards_intact(view, full), f"case {k}: guard written"
+    for n, (view, full) in params.items():
+        if view is not None:
+            assert guards_intact(view, full), f"case {k}: {n} guard written"
+            assert np.array_equal(view.cpu().numpy().view(np.uint32), d[n].view(np.uint32)), f"case {k}: {n} written"
     got = [v.cpu().numpy() for v, _ in outs]
     what = f"case {k} {op} {rows}x{cols} {policy}"
     gam, bet = d.get("gamma"), d.get("beta")
@@ -158,7 +202,7 @@ def test_random_case(k):
         if c["with_sum"]:
             bits_equal(got[1], comb.astype(np.float32), what + " sum_out")
         if policy == "unordered_tree":
-            assert_parity(got[0], ref, what)
+            assert_layernorm(got[0], ref, comb, gam, EPS[op], what)
         else:
             bits_equal(got[0], oracle.layernorm_ordered_f32(comb, gam, bet, EPS[op], policy), what)
         return
@@ -183,7 +227,10 @@ def test_random_case(k):
     else:
         ref = oracle.layernorm(x, gam, bet, EPS[op])
     if policy == "unordered_tree":
-        assert_parity(got[0], ref, what)
+        if op == "layernorm":
+            assert_layernorm(got[0], ref, x, gam, EPS[op], what)
+        else:
+            assert_parity(got[0], ref, what)
         return
     g = ordered_bound(op, policy, cols)
     err = np.abs(got[0].astype(np.float64) - ref)
