@@ -45,7 +45,13 @@
  *           reported and the result is unspecified (it may differ between
  *           policies and plans).  For lr_row_minmax_f32 in particular, a
  *           NaN element may be skipped or returned depending on the
- *           policy.
+ *           policy.  RMSNorm and LayerNorm square the elements in FP32:
+ *           with eps = 0 (or eps far below the row's mean square or
+ *           variance), a row whose magnitude is below about 1e-20 loses
+ *           accuracy to the subnormal range, and one whose squares all
+ *           round to zero (below about 1e-23) gives +-infinity or NaN, as
+ *           the FP32 formula does.  Rows down to about 1e-19 (squares and
+ *           mean square subnormal) keep the stated accuracy.
  * Threads.  All entry points are thread-safe.
  * Policy.   See lr_reduction_policy below: LR_UNORDERED_TREE lets every
  *           add fold be reassociated; the three ordered policies fix the

@@ -254,7 +254,16 @@ __device__ __forceinline__ float div_rowsum(float a, float s, float y) {
 constexpr unsigned kRowsumTiny = 0x0F7FFFFFu;  // bits(2^-96) - 1
 __device__ __forceinline__ unsigned rowsum_guard(float a) { return __float_as_uint(a) - 1u; }
 
-__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+// 1/sqrt(x) to about one ulp with the hardware reciprocal square root, which
+// takes a subnormal argument as zero and returns +inf.  An argument below
+// 2^-126 (eps = 0 and a row whose mean square or variance is subnormal) is
+// scaled by 2^24 into the normal range first and the result by 2^12; both
+// scalings are exact.
+__device__ __forceinline__ float fast_rsqrt(float x) {
+    const bool sub = x < 0x1p-126f;
+    const float r = __builtin_amdgcn_rsqf(sub ? x * 0x1p24f : x);
+    return sub ? r * 0x1p12f : r;
+}
 
 // Softmax state over a row team with one exchange: every wave brings its
 // own (max m_w, sum of exp(x - m_w)) pair, lane 0 publishes it, one workgroup
