@@ -28,6 +28,10 @@ COMMON = [
     # no packed-FP32 VALU instructions (v_pk_add/mul/fma_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # the first nine kernel arguments (the row-addressing fields every
+    # kernel entry takes ahead of its KArgs, csrc/lr_entry.hpp) arrive
+    # preloaded in scalar registers at wave launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=9",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
 

@@ -5,7 +5,8 @@
 // and no parameter read between the two.  SYNC: every wave waits for its
 // reads and the workgroup meets at one barrier before the first store, as
 // the reductions' cross-wave exchange makes them do; without it each wave
-// stores as soon as its own reads land.
+// stores as soon as its own reads land.  Its four arguments arrive
+// preloaded in scalar registers, as the operations' leading arguments do.
 #include "lr_device.hpp"
 #include "lr_internal.hpp"
 

@@ -28,6 +28,7 @@
 #pragma clang fp contract(off)
 
 #include "lr_device.hpp"
+#include "lr_entry.hpp"
 #include "lr_internal.hpp"
 
 namespace lr {
@@ -240,7 +241,8 @@ __device__ __forceinline__ float ordered_sum(const float* xr, const float* rr, i
 }
 
 template <int OP, int POL>
-__global__ void __launch_bounds__(1024) k_ordered(const KArgs a) {
+__global__ void __launch_bounds__(1024) k_ordered(LR_ENTRY_PARAMS) {
+    const KArgs a = LR_ENTRY_KARGS;
     __shared__ __attribute__((aligned(16))) float slabs[kMaxWaves][kSlab];
     __shared__ float stacks[kMaxWaves][kTreeStack];
     const int lane = (int)threadIdx.x % kWave;
@@ -370,13 +372,13 @@ template <int POL>
 hipError_t launch_ordered_pol(int op, const KArgs& a, const lr_plan& p, hipStream_t s) {
     const dim3 grid((unsigned)p.blocks), block(p.threads_per_block);
     switch (op) {
-        case kSoftmax: hipLaunchKernelGGL((k_ordered<kSoftmax, POL>), grid, block, 0, s, a); break;
-        case kRmsNorm: hipLaunchKernelGGL((k_ordered<kRmsNorm, POL>), grid, block, 0, s, a); break;
-        case kLayerNorm: hipLaunchKernelGGL((k_ordered<kLayerNorm, POL>), grid, block, 0, s, a); break;
-        case kCrossEntropy: hipLaunchKernelGGL((k_ordered<kCrossEntropy, POL>), grid, block, 0, s, a); break;
-        case kAddLayerNorm: hipLaunchKernelGGL((k_ordered<kAddLayerNorm, POL>), grid, block, 0, s, a); break;
-        case kRowSum: hipLaunchKernelGGL((k_ordered<kRowSum, POL>), grid, block, 0, s, a); break;
-        case kRowMinMax: hipLaunchKernelGGL((k_ordered<kRowMinMax, POL>), grid, block, 0, s, a); break;
+        case kSoftmax: hipLaunchKernelGGL((k_ordered<kSoftmax, POL>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case kRmsNorm: hipLaunchKernelGGL((k_ordered<kRmsNorm, POL>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case kLayerNorm: hipLaunchKernelGGL((k_ordered<kLayerNorm, POL>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case kCrossEntropy: hipLaunchKernelGGL((k_ordered<kCrossEntropy, POL>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case kAddLayerNorm: hipLaunchKernelGGL((k_ordered<kAddLayerNorm, POL>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case kRowSum: hipLaunchKernelGGL((k_ordered<kRowSum, POL>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case kRowMinMax: hipLaunchKernelGGL((k_ordered<kRowMinMax, POL>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

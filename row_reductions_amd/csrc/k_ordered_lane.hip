@@ -14,6 +14,7 @@
 #pragma clang fp contract(off)
 
 #include "lr_device.hpp"
+#include "lr_entry.hpp"
 #include "lr_internal.hpp"
 
 namespace lr {
@@ -270,7 +271,8 @@ __device__ __forceinline__ void lane_body(const KArgs& a, float* tile) {
 }
 
 template <int OP, int POL, int N4>
-__global__ void __launch_bounds__(64) k_ordered_lane(const KArgs a) {
+__global__ void __launch_bounds__(64) k_ordered_lane(LR_ENTRY_PARAMS) {
+    const KArgs a = LR_ENTRY_KARGS;
     __shared__ float tile[lane_tile_floats<4 * N4>()];
     if (a.cols == 4 * N4) {
         lane_body<OP, POL, N4, true>(a, tile);
@@ -283,11 +285,11 @@ template <int OP, int POL>
 hipError_t launch_lane_n4(const KArgs& a, const lr_plan& p, hipStream_t s) {
     const dim3 grid((unsigned)p.blocks), block(p.threads_per_block);
     switch (p.chunks_per_lane) {
-        case 1: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 2>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 4>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 8>), grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 16>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 1>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case 2: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 2>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case 4: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 4>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case 8: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 8>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
+        case 16: hipLaunchKernelGGL((k_ordered_lane<OP, POL, 16>), grid, block, 0, s, LR_ENTRY_ARGS(a)); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

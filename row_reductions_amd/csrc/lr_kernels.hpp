@@ -17,6 +17,7 @@
 #pragma once
 
 #include "lr_device.hpp"
+#include "lr_entry.hpp"
 #include "lr_internal.hpp"
 
 namespace lr {
@@ -560,17 +561,17 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[2][kMaxW
 
 template <int OP, int NCH, bool AL, int PM>
 __global__ void __launch_bounds__(cache_max_threads(NCH))
-k_cache(const KArgs a) {
+k_cache(LR_ENTRY_PARAMS) {
     __shared__ float red[2][kMaxWaves];
-    cache_body<OP, NCH, AL, PM, kWave>(a, red);
+    cache_body<OP, NCH, AL, PM, kWave>(LR_ENTRY_KARGS, red);
 }
 
 // Sub-wave teams: LW lanes per row, 64 / LW rows per wave, S = 1.
 template <int OP, int NCH, bool AL, int PM, int LW>
 __global__ void __launch_bounds__(1024)
-k_cache_narrow(const KArgs a) {
+k_cache_narrow(LR_ENTRY_PARAMS) {
     __shared__ float red[2][kMaxWaves];  // untouched: no cross-wave exchange
-    cache_body<OP, NCH, AL, PM, LW>(a, red);
+    cache_body<OP, NCH, AL, PM, LW>(LR_ENTRY_KARGS, red);
 }
 
 // ===========================================================================
@@ -595,7 +596,8 @@ __device__ __forceinline__ void load_trip(float4 (&v)[kStreamUnroll], const floa
 }
 
 template <int OP, bool AL>
-__global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
+__global__ void __launch_bounds__(1024) k_stream(LR_ENTRY_PARAMS) {
+    const KArgs a = LR_ENTRY_KARGS;
     __shared__ float red[2][kMaxWaves];
     constexpr int U = kStreamUnroll;
     constexpr float ID = op_identity<OP>();
@@ -759,14 +761,15 @@ __global__ void __launch_bounds__(1024) k_stream(const KArgs a) {
 // ---------------------------------------------------------------------------
 template <int OP, int NCH, bool AL, int PM>
 hipError_t launch_cache_inst(const KArgs& a, const lr_plan& p, hipStream_t s) {
-    hipLaunchKernelGGL((k_cache<OP, NCH, AL, PM>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+    hipLaunchKernelGGL((k_cache<OP, NCH, AL, PM>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s,
+                       LR_ENTRY_ARGS(a));
     return hipGetLastError();
 }
 
 template <int OP, int NCH, bool AL, int PM, int LW>
 hipError_t launch_narrow_inst(const KArgs& a, const lr_plan& p, hipStream_t s) {
     hipLaunchKernelGGL((k_cache_narrow<OP, NCH, AL, PM, LW>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0,
-                       s, a);
+                       s, LR_ENTRY_ARGS(a));
     return hipGetLastError();
 }
 
@@ -824,9 +827,11 @@ hipError_t launch_op(const KArgs& a, const lr_plan& p, bool aligned, hipStream_t
     }
     if (p.family == LR_FAMILY_STREAM) {
         if (aligned)
-            hipLaunchKernelGGL((k_stream<OP, true>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+            hipLaunchKernelGGL((k_stream<OP, true>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s,
+                               LR_ENTRY_ARGS(a));
         else
-            hipLaunchKernelGGL((k_stream<OP, false>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+            hipLaunchKernelGGL((k_stream<OP, false>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s,
+                               LR_ENTRY_ARGS(a));
         return hipGetLastError();
     }
     return hipErrorInvalidValue;

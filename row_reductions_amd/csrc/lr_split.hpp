@@ -94,7 +94,8 @@ __device__ __forceinline__ void load_segment(const KArgs& a, const SplitCtx& c, 
 }
 
 template <int OP, int NCH, bool AL>
-__global__ void __launch_bounds__(1024) k_split_stats(const KArgs a) {
+__global__ void __launch_bounds__(1024) k_split_stats(LR_ENTRY_PARAMS) {
+    const KArgs a = LR_ENTRY_KARGS;
     __shared__ float red[2][kMaxWaves];
     constexpr float ID = op_identity<OP>();
     const int S = a.S;
@@ -214,7 +215,8 @@ __device__ __forceinline__ RowStats merge_partials(const KArgs& a, Partial q, in
 }
 
 template <int OP, int NCH, bool AL, int PM>
-__global__ void __launch_bounds__(1024) k_split_apply(const KArgs a) {
+__global__ void __launch_bounds__(1024) k_split_apply(LR_ENTRY_PARAMS) {
+    const KArgs a = LR_ENTRY_KARGS;
     constexpr int NP = num_params<OP>();
     const int S = a.S;
     const int W = kWave * S;
@@ -280,7 +282,8 @@ __global__ void __launch_bounds__(1024) k_split_apply(const KArgs a) {
 constexpr int kMergeWaves = 4;
 
 template <int OP>
-__global__ void __launch_bounds__(kMergeWaves * kWave) k_split_merge(const KArgs a) {
+__global__ void __launch_bounds__(kMergeWaves * kWave) k_split_merge(LR_ENTRY_PARAMS) {
+    const KArgs a = LR_ENTRY_KARGS;
     const int lane = (int)threadIdx.x & (kWave - 1);
     const int64_t row = (int64_t)blockIdx.x * kMergeWaves + wave_id();
     if (row >= a.rows) return;  // whole waves leave; this kernel has no barrier
@@ -305,14 +308,14 @@ __global__ void __launch_bounds__(kMergeWaves * kWave) k_split_merge(const KArgs
 template <int OP, int NCH, bool AL, int PM>
 hipError_t launch_split_inst(const KArgs& a, const lr_plan& p, hipStream_t s) {
     const dim3 grid((unsigned)p.blocks), block(p.threads_per_block);
-    hipLaunchKernelGGL((k_split_stats<OP, NCH, AL>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_split_stats<OP, NCH, AL>), grid, block, 0, s, LR_ENTRY_ARGS(a));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (OP == kCrossEntropy || OP == kRowSum || OP == kRowMinMax) {
         const unsigned mb = (unsigned)((a.rows + kMergeWaves - 1) / kMergeWaves);
-        hipLaunchKernelGGL((k_split_merge<OP>), dim3(mb), dim3(kMergeWaves * kWave), 0, s, a);
+        hipLaunchKernelGGL((k_split_merge<OP>), dim3(mb), dim3(kMergeWaves * kWave), 0, s, LR_ENTRY_ARGS(a));
     } else {
-        hipLaunchKernelGGL((k_split_apply<OP, NCH, AL, PM>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_split_apply<OP, NCH, AL, PM>), grid, block, 0, s, LR_ENTRY_ARGS(a));
     }
     return hipGetLastError();
 }

@@ -247,31 +247,33 @@ __device__ __forceinline__ void tree_body(const KArgs& a, float (&red)[2][kMaxWa
 
 template <int OP, int NCH, bool AL, int PM>
 __global__ void __launch_bounds__(cache_max_threads(NCH))
-k_tree(const KArgs a) {
+k_tree(LR_ENTRY_PARAMS) {
     __shared__ float red[2][kMaxWaves];
     __shared__ float tsl[2][kMaxWaves][kTreeMaxSlabs];
-    tree_body<OP, NCH, AL, PM, kWave>(a, red, tsl);
+    tree_body<OP, NCH, AL, PM, kWave>(LR_ENTRY_KARGS, red, tsl);
 }
 
 // Sub-wave teams: LW lanes per row, one chunk per lane, 64 / LW rows per wave.
 template <int OP, bool AL, int PM, int LW>
 __global__ void __launch_bounds__(1024)
-k_tree_narrow(const KArgs a) {
+k_tree_narrow(LR_ENTRY_PARAMS) {
     __shared__ float red[2][kMaxWaves];               // untouched: no cross-wave exchange
     __shared__ float tsl[2][kMaxWaves][kTreeMaxSlabs];  // untouched
-    tree_body<OP, 1, AL, PM, LW>(a, red, tsl);
+    tree_body<OP, 1, AL, PM, LW>(LR_ENTRY_KARGS, red, tsl);
 }
 
 template <int OP, int NCH, bool AL, int PM>
 hipError_t launch_tree_inst(const KArgs& a, const lr_plan& p, hipStream_t s) {
-    hipLaunchKernelGGL((k_tree<OP, NCH, AL, PM>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+    hipLaunchKernelGGL((k_tree<OP, NCH, AL, PM>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s,
+                       LR_ENTRY_ARGS(a));
     return hipGetLastError();
 }
 
 template <int OP, bool AL, int PM, int LW>
 hipError_t launch_tree_narrow(const KArgs& a, const lr_plan& p, hipStream_t s) {
     if (p.chunks_per_lane != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_tree_narrow<OP, AL, PM, LW>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s, a);
+    hipLaunchKernelGGL((k_tree_narrow<OP, AL, PM, LW>), dim3((unsigned)p.blocks), dim3(p.threads_per_block), 0, s,
+                       LR_ENTRY_ARGS(a));
     return hipGetLastError();
 }
 

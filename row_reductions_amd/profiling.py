@@ -30,9 +30,13 @@ OP_NAMES = {0: "softmax", 1: "rmsnorm", 2: "layernorm", 3: "cross_entropy"}
 
 def csrc_hash() -> str:
     """sha256 over the device sources: the `.hip` translation units and the
-    `.hpp` headers (names and contents).  Host-only files (the C ABI, the
-    planner and its table) do not change a kernel."""
+    `.hpp` headers (names and contents), and the compiler flags they are
+    built with (include paths left out: they name the checkout).  Host-only
+    files (the C ABI, the planner and its table) do not change a kernel."""
+    from . import build as _build
     h = hashlib.sha256()
+    flags = [f for f in _build.COMMON if not f.startswith("-I")]
+    h.update(repr((flags, sorted(_build.EXTRA.items()))).encode())
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".hpp")):
             h.update(name.encode())
