@@ -85,6 +85,21 @@ LR_HD bool chunk_full(int k, int phase, int cols) {
     return kVec * k - phase >= 0 && kVec * k + kVec - phase <= cols;
 }
 
+// Elements of a row (phase, cols) held by wavefront s of a whole-wave team
+// of W = 64 S workers with nch chunks each: its stripe slot c covers grid
+// positions 4 b .. 4 b + 255, b = 64 s + W c, and the row occupies grid
+// positions phase .. phase + cols - 1.
+LR_HD int wave_elems(int s, int W, int nch, int phase, int cols) {
+    int n = 0;
+    for (int c = 0; c < nch; ++c) {
+        const int p = kVec * (s * kWave + W * c);
+        const int lo = p > phase ? p : phase;
+        const int hi = p + kVec * kWave < phase + cols ? p + kVec * kWave : phase + cols;
+        n += hi > lo ? hi - lo : 0;
+    }
+    return n;
+}
+
 // Split family: a row's nv chunks are cut into G segments of L = ceil(nv/G)
 // chunks; segment g holds chunks [k0, k1) (the last ones may be short or
 // empty).  Worker w of the segment's workgroup owns chunks k0 + w + W*c.
