@@ -581,9 +581,9 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[4][kMaxW
             __syncthreads();
             const bool in = t.lane < S;
             const float4 e = in ? slot[t.q * S + t.lane] : splat4(0.0f);
-            const float mu = wave_allreduce<AddOp>(__builtin_fmaf(e.w, e.x, e.z)) * a.inv_cols;
+            const float mu = team_merge<AddOp>(__builtin_fmaf(e.w, e.x, e.z)) * a.inv_cols;
             const float dw = e.x - mu;
-            qs = wave_allreduce<AddOp>(in ? e.y + dw * (2.0f * e.z + e.w * dw) : 0.0f);
+            qs = team_merge<AddOp>(in ? e.y + dw * (2.0f * e.z + e.w * dw) : 0.0f);
 #pragma unroll
             for (int c = 0; c < NCH; ++c) v[c] = make_float4(v[c].x - mu, v[c].y - mu, v[c].z - mu, v[c].w - mu);
         }
