@@ -154,14 +154,20 @@ def trace_runs(trace_csv: str, min_dispatches: int = 100) -> list[dict]:
     return out
 
 
+# Parameter list of every kernel entry (csrc/lr_entry.hpp), as demangled:
+# the nine preloaded leading arguments, then KArgs.
+ENTRY_PARAMS = ("(float const*, long, int, int, int, int, float const*, float const*, float const*, "
+                "lr::KArgs)")
+
+
 def kernel_name(op_index: int, plan, aligned: bool, param_mode: int) -> str | None:
     """The demangled name of the kernel instance a CACHE or STREAM plan
     launches (param_mode: 0 no gamma/beta, 1 all present, 2 some)."""
     al = "true" if aligned else "false"
     if plan.family == 0:
-        return f"void lr::k_cache<{op_index}, {plan.chunks_per_lane}, {al}, {param_mode}>(lr::KArgs)"
+        return f"void lr::k_cache<{op_index}, {plan.chunks_per_lane}, {al}, {param_mode}>" + ENTRY_PARAMS
     if plan.family == 1:
-        return f"void lr::k_stream<{op_index}, {al}>(lr::KArgs)"
+        return f"void lr::k_stream<{op_index}, {al}>" + ENTRY_PARAMS
     return None
 
 

@@ -9,6 +9,8 @@ import pytest
 import row_reductions_amd as lr
 from row_reductions_amd import profiling
 
+# the demangled parameter list of every kernel entry
+ENTRY = "(float const*, long, int, int, int, int, float const*, float const*, float const*, lr::KArgs)"
 SUMMARY = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles",
                        "hbm_traffic_768x6144.json")
 
@@ -17,9 +19,9 @@ def test_kernel_names_follow_the_plan():
     F = lr.lr_device_facts_mi355x()
     p = lr.lr_plan_for_device(F, "rmsnorm", 768, 6144, "unordered_tree", 1)
     p.family, p.chunks_per_lane = lr.LR_FAMILY_CACHE, 3
-    assert profiling.kernel_name(1, p, True, 1) == "void lr::k_cache<1, 3, true, 1>(lr::KArgs)"
+    assert profiling.kernel_name(1, p, True, 1) == "void lr::k_cache<1, 3, true, 1>" + ENTRY
     p.family = lr.LR_FAMILY_STREAM
-    assert profiling.kernel_name(0, p, False, 0) == "void lr::k_stream<0, false>(lr::KArgs)"
+    assert profiling.kernel_name(0, p, False, 0) == "void lr::k_stream<0, false>" + ENTRY
     p.family = lr.LR_FAMILY_SPLIT
     assert profiling.kernel_name(0, p, True, 0) is None
 
@@ -28,10 +30,10 @@ def test_lookup_requires_matching_sources_and_instance(tmp_path):
     rec = {"op": "softmax", "traffic_bytes": 1.0}
     good = tmp_path / "good.json"
     good.write_text(json.dumps({"csrc_sha256": profiling.csrc_hash(),
-                                "kernels": {"void lr::k_cache<0, 6, true, 0>(lr::KArgs)": rec}}))
+                                "kernels": {"void lr::k_cache<0, 6, true, 0>" + ENTRY: rec}}))
     assert profiling.lookup(str(good), "softmax")["traffic_bytes"] == 1.0
-    assert profiling.lookup(str(good), "softmax", "void lr::k_cache<0, 6, true, 0>(lr::KArgs)") is not None
-    assert profiling.lookup(str(good), "softmax", "void lr::k_cache<0, 4, true, 0>(lr::KArgs)") is None
+    assert profiling.lookup(str(good), "softmax", "void lr::k_cache<0, 6, true, 0>" + ENTRY) is not None
+    assert profiling.lookup(str(good), "softmax", "void lr::k_cache<0, 4, true, 0>" + ENTRY) is None
     assert profiling.lookup(str(good), "rmsnorm") is None
     stale = tmp_path / "stale.json"
     stale.write_text(json.dumps({"csrc_sha256": "0" * 64, "kernels": {"k": rec}}))
