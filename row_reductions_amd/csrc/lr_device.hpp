@@ -76,6 +76,33 @@ __device__ __forceinline__ float wave_allreduce(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
+// Two independent wave64 all-reduces taken step by step side by side, so
+// that each step's cross-lane moves of the two values overlap instead of
+// running one whole chain after the other.  Same bits as two calls.
+template <class R>
+__device__ __forceinline__ void wave_allreduce2(float& a, float& b) {
+    a = R::apply(a, dpp_mov<0xB1>(a));
+    b = R::apply(b, dpp_mov<0xB1>(b));
+    a = R::apply(a, dpp_mov<0x4E>(a));
+    b = R::apply(b, dpp_mov<0x4E>(b));
+    a = R::apply(a, dpp_mov<0x141>(a));
+    b = R::apply(b, dpp_mov<0x141>(b));
+    a = R::apply(a, dpp_mov<0x140>(a));
+    b = R::apply(b, dpp_mov<0x140>(b));
+    const unsigned ua = __builtin_bit_cast(unsigned, a), ub = __builtin_bit_cast(unsigned, b);
+    auto pa = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
+    auto pb = __builtin_amdgcn_permlane16_swap(ub, ub, false, false);
+    a = R::apply(__builtin_bit_cast(float, (unsigned)pa[0]), __builtin_bit_cast(float, (unsigned)pa[1]));
+    b = R::apply(__builtin_bit_cast(float, (unsigned)pb[0]), __builtin_bit_cast(float, (unsigned)pb[1]));
+    const unsigned va = __builtin_bit_cast(unsigned, a), vb = __builtin_bit_cast(unsigned, b);
+    auto qa = __builtin_amdgcn_permlane32_swap(va, va, false, false);
+    auto qb = __builtin_amdgcn_permlane32_swap(vb, vb, false, false);
+    a = R::apply(__builtin_bit_cast(float, (unsigned)qa[0]), __builtin_bit_cast(float, (unsigned)qa[1]));
+    b = R::apply(__builtin_bit_cast(float, (unsigned)qb[0]), __builtin_bit_cast(float, (unsigned)qb[1]));
+    a = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a)));
+    b = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, b)));
+}
+
 // All-reduce over aligned groups of L lanes (L = 4, 8, 16, 32 or 64): the
 // first log2(L) steps of the wave64 all-reduce above, after which every lane
 // of a group holds the group's total (with the same bits in every lane of

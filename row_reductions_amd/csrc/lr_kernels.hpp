@@ -562,17 +562,22 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[4][kMaxW
             // the other: one workgroup barrier less (LayerNorm 768 x 6144 at
             // six waves per row on MI355X: 6.78 -> 6.74 us).
             const float sw = wave_allreduce<AddOp>(sum);
-            const int nw = active ? wave_elems(t.s, W, NCH, h, cols) : 0;
-            const float mw = nw > 0 ? sw / (float)nw : 0.0f;
-            float q = 0.0f, cw = 0.0f;
             // aligned rows: a wave whose every slot lies inside the row (its
             // last chunk, t.s * 64 + 63 + W * (NCH - 1), below nv; a
-            // wave-uniform test) centres without the per-element selects
-            // that zero the slots past the row.  Same-box A/B on MI355X:
-            // 768 x 6144 6.73 -> 6.71 us, 1024 x 4096 6.57 -> 6.52, 512 x
-            // 12288 8.95 -> 8.87, 2048 x 8192 25.23 -> 25.16.
+            // wave-uniform test) holds exactly 256 NCH elements, which it
+            // centres without the per-element selects that zero the slots
+            // past the row; when that count is a power of two its mean is a
+            // multiply, which equals the division bit for bit.  Same-box A/B
+            // on MI355X for the selects: 768 x 6144 6.73 -> 6.71 us, 1024 x
+            // 4096 6.57 -> 6.52, 512 x 12288 8.95 -> 8.87, 2048 x 8192 25.23 ->
+            // 25.16.
+            constexpr int kInside = kWave * kVec * NCH;
             const bool inside = AL && t.s * kWave + kWave - 1 + W * (NCH - 1) < nv;
+            int nw;
+            float mw, q = 0.0f, cw = 0.0f;
             if (inside) {
+                nw = kInside;
+                mw = (kInside & (kInside - 1)) == 0 ? sw * (1.0f / kInside) : sw / (float)kInside;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     const float4 d = make_float4(v[c].x - mw, v[c].y - mw, v[c].z - mw, v[c].w - mw);
@@ -580,6 +585,8 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[4][kMaxW
                     cw += (d.x + d.y) + (d.z + d.w);
                 }
             } else {
+                nw = active ? wave_elems(t.s, W, NCH, h, cols) : 0;
+                mw = nw > 0 ? sw / (float)nw : 0.0f;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     const int k = chunk(c);
@@ -590,8 +597,7 @@ __device__ __forceinline__ void cache_body(const KArgs& a, float (&red)[4][kMaxW
                     cw += (d.x + d.y) + (d.z + d.w);
                 }
             }
-            q = wave_allreduce<AddOp>(q);
-            cw = wave_allreduce<AddOp>(cw);
+            wave_allreduce2<AddOp>(q, cw);
             float4* slot = reinterpret_cast<float4*>(&red[0][0]);
             if (t.lane == 0) slot[t.q * S + t.s] = make_float4(mw, q, cw, (float)nw);
             __syncthreads();
