@@ -131,6 +131,26 @@ def trace_fraction(lr, op: str, nbytes: int) -> dict:
             "trace_dispatches": rec["dispatches"]}
 
 
+def device_record(lr, torch) -> dict:
+    """The device the figures were taken on: its name, compute units, and the
+    memory clock and bus width the runtime reports.  The fractions divide by
+    the published 8 TB/s; over the reported bus that is the per-pin rate
+    given here (HBM3E moves several bits per pin per reported clock)."""
+    props = torch.cuda.get_device_properties(0)
+    rec = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+           "compute_units": props.multi_processor_count, "hbm_peak_used_gbs": HBM_PEAK_GBS}
+    try:
+        clk_khz, bus_bits = lr.lr_device_memory_query()
+    except lr.LrError:
+        return rec
+    rec.update({"memory_clock_khz": clk_khz, "memory_bus_bits": bus_bits})
+    if bus_bits > 0 and clk_khz > 0:
+        gbps_per_pin = HBM_PEAK_GBS * 8 / bus_bits
+        rec.update({"peak_per_pin_gbps": round(gbps_per_pin, 3),
+                    "peak_transfers_per_reported_clock": round(gbps_per_pin * 1e9 / (clk_khz * 1e3), 3)})
+    return rec
+
+
 def op_bytes(rows: int, cols: int) -> int:
     """Algorithmic bytes of one softmax / norm launch: read + write of the tensor."""
     return 2 * rows * cols * 4
@@ -304,6 +324,7 @@ def main():
         "gbps_per_op": {op: round(gbps[op], 1) for op in OPS},
         "pct_of_hbm_peak_per_op": {op: round(100 * gbps[op] / HBM_PEAK_GBS, 2) for op in OPS},
         "plans": plans,
+        "device": device_record(lr, torch),
         "roofline": {
             "kernel": dominant,
             "bound": "hbm",

@@ -429,6 +429,12 @@ lr_status lr_device_facts_query(lr_device_facts* out);
 /* Facts of an MI355X, for planning without a device. */
 void lr_device_facts_mi355x(lr_device_facts* out);
 
+/* The current HIP device's memory clock (kHz) and memory bus width (bits),
+ * as the runtime reports them, so that a measurement can state the device it
+ * ran on beside the peak bandwidth it divides by.  NULL outputs:
+ * LR_ERR_NULL_POINTER; no usable device: LR_ERR_HIP. */
+lr_status lr_device_memory_query(int32_t* clock_khz, int32_t* bus_width_bits);
+
 /* The plan an operation launches with on the current device, assuming
  * 16-byte aligned tensor bases. */
 lr_status lr_plan_query(lr_op op, int64_t rows, int64_t cols,

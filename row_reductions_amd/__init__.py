@@ -129,6 +129,7 @@ def _load():
         "lr_row_sum_f32_with_plan": [P, P, I64, I64, I32, PP, P],
         "lr_row_minmax_f32_with_plan": [P, P, P, I64, I64, I32, PP, P],
         "lr_device_facts_query": [PF],
+        "lr_device_memory_query": [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)],
         "lr_plan_query": [I32, I64, I64, I32, PP],
         "lr_plan_for_device": [PF, I32, I64, I64, I32, I32, PP],
         "lr_plan_enumerate": [PF, I32, I64, I64, I32, I32, PP, I32, ctypes.POINTER(I32)],
@@ -343,6 +344,15 @@ def lr_device_facts_query() -> LrDeviceFacts:
     if st != LR_OK:
         raise LrError(st, "lr_device_facts_query")
     return f
+
+
+def lr_device_memory_query() -> tuple:
+    """(memory clock in kHz, memory bus width in bits) of the current device."""
+    clk, bus = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib.lr_device_memory_query(ctypes.byref(clk), ctypes.byref(bus))
+    if st != LR_OK:
+        raise LrError(st, "lr_device_memory_query")
+    return clk.value, bus.value
 
 
 def lr_plan_query(op, rows, cols, policy=LR_UNORDERED_TREE) -> LrPlan:

@@ -500,6 +500,18 @@ lr_status lr_device_facts_query(lr_device_facts* out) {
     return lr::current_facts(out);
 }
 
+lr_status lr_device_memory_query(int32_t* clock_khz, int32_t* bus_width_bits) {
+    if (clock_khz == nullptr || bus_width_bits == nullptr) return LR_ERR_NULL_POINTER;
+    int dev = 0, clk = 0, bus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&clk, hipDeviceAttributeMemoryClockRate, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&bus, hipDeviceAttributeMemoryBusWidth, dev) != hipSuccess)
+        return LR_ERR_HIP;
+    *clock_khz = clk;
+    *bus_width_bits = bus;
+    return LR_OK;
+}
+
 lr_status lr_plan_query(lr_op op, int64_t rows, int64_t cols, lr_reduction_policy policy, lr_plan* out) {
     if (out == nullptr) return LR_ERR_NULL_POINTER;
     lr_device_facts f;

@@ -227,3 +227,14 @@ def test_copy_rows_validates_before_any_hip_call():
     big = next(q for q in lr.lr_plan_enumerate(F, "softmax", 4, 32768, "unordered_tree", 1)
                if q.family == lr.LR_FAMILY_CACHE and q.chunks_per_lane == 16)
     assert lr.lr_copy_rows_f32(X, Y, 4, 32768, big, 1, 0) == lr.LR_ERR_UNREALIZABLE_PLAN
+
+
+def test_device_memory_query_checks_its_outputs():
+    import ctypes
+    v = ctypes.c_int32(0)
+    assert lr.lib.lr_device_memory_query(None, ctypes.byref(v)) == lr.LR_ERR_NULL_POINTER
+    assert lr.lib.lr_device_memory_query(ctypes.byref(v), None) == lr.LR_ERR_NULL_POINTER
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is present")
+    with pytest.raises(lr.LrError):
+        lr.lr_device_memory_query()
