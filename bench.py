@@ -359,6 +359,22 @@ def main():
                 extra[f"{op}_768x6144_{pname}_cold"] = {"us_per_op": round(t["median"], 3),
                                                         "range": [round(t["min"], 3), round(t["max"], 3)],
                                                         "gbps": round(b / t["median"] / 1e3, 1)}
+        # the norms called without their parameters (cold): a plan of their own
+        for op in ("rmsnorm", "layernorm"):
+            def bare(i, op=op):
+                k = i % nsets
+                if op == "rmsnorm":
+                    st = lr.lib.lr_rmsnorm_f32(rx[k].data_ptr(), None, ry[k].data_ptr(), ROWS, COLS,
+                                               EPS["rmsnorm"], lr.LR_UNORDERED_TREE, sh)
+                else:
+                    st = lr.lib.lr_layernorm_f32(lx[k].data_ptr(), None, None, ly[k].data_ptr(), ROWS, COLS,
+                                                 EPS["layernorm"], lr.LR_UNORDERED_TREE, sh)
+                if st != 0:
+                    raise lr.LrError(st, op)
+            t = time_batches(torch, stream, bare, samples=5)
+            extra[f"{op}_768x6144_no_params_cold"] = {"us_per_op": round(t["median"], 3),
+                                                      "range": [round(t["min"], 3), round(t["max"], 3)],
+                                                      "gbps": round(b / t["median"] / 1e3, 1)}
         progress("warm-cache and ordered-policy figures done")
         extra.update(add_layernorm_extra(lr, synth, torch, dev, sh, stream, nsets))
         extra.update(small_configs_graph(lr, synth, torch, dev))

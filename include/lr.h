@@ -436,13 +436,15 @@ void lr_device_facts_mi355x(lr_device_facts* out);
 lr_status lr_device_memory_query(int32_t* clock_khz, int32_t* bus_width_bits);
 
 /* The plan an operation launches with on the current device, assuming
- * 16-byte aligned tensor bases. */
+ * 16-byte aligned tensor bases and, for RMSNorm and LayerNorm, gamma or beta
+ * given (a norm called without both may take a plan measured for that case). */
 lr_status lr_plan_query(lr_op op, int64_t rows, int64_t cols,
                         lr_reduction_policy policy, lr_plan* out);
 
 /* Pure planner: the automatic plan for `facts`.  row_aligned = 1 when every
  * row starts 16-byte aligned (cols % 4 == 0 and aligned bases).  Never a
- * SPLIT plan (the typed entry points have no workspace). */
+ * SPLIT plan (the typed entry points have no workspace).  For RMSNorm and
+ * LayerNorm, the plan of a call that gives gamma or beta. */
 lr_status lr_plan_for_device(const lr_device_facts* facts, lr_op op, int64_t rows,
                              int64_t cols, lr_reduction_policy policy,
                              int32_t row_aligned, lr_plan* out);

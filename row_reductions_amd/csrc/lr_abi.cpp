@@ -15,6 +15,12 @@ namespace lr {
 
 lr_status validate_plan(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy,
                         bool aligned, const lr_plan* p);
+// The automatic plan of a call (lr_planner.cpp): lr_plan_for_device, or with
+// allow_split the plan of lr_plan_for_device_ws, where `params` says whether
+// a norm's call gives gamma or beta; without them a norm may take a plan the
+// table lists for that case.
+lr_status plan_for_call(const lr_device_facts* facts, int op, int64_t rows, int64_t cols, int policy,
+                        bool row_aligned, bool allow_split, bool params, lr_plan* out);
 
 namespace {
 
@@ -225,18 +231,19 @@ lr_status run(const Call& c, const lr_plan* forced, hipStream_t stream) {
         plan = *forced;
     } else {
         // with a workspace large enough, the plan that may split rows;
-        // otherwise the typed entry points' plan
+        // otherwise the typed entry points' plan.  A norm called without
+        // gamma and beta may have a plan of its own for that case.
+        const bool params = c.gamma != nullptr || c.beta != nullptr;
         bool split_ok = false;
         if (have_ws) {
             lr_plan w;
-            split_ok = lr_plan_for_device_ws(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
-                                             rows_aligned ? 1 : 0, &w) == LR_OK &&
+            split_ok = plan_for_call(&facts, c.op, c.rows, c.cols, c.policy, rows_aligned, true, params, &w) ==
+                           LR_OK &&
                        c.workspace_bytes >= (uint64_t)plan_workspace_bytes(w, c.rows);
             if (split_ok) plan = w;
         }
         if (!split_ok) {
-            st = lr_plan_for_device(&facts, (lr_op)c.op, c.rows, c.cols, (lr_reduction_policy)c.policy,
-                                    rows_aligned ? 1 : 0, &plan);
+            st = plan_for_call(&facts, c.op, c.rows, c.cols, c.policy, rows_aligned, false, params, &plan);
             if (st != LR_OK) return st;
         }
     }

@@ -299,6 +299,7 @@ struct TableEntry {
     int family, S, Q, nch;
     int splits;  // SPLIT entries only
     int lanes;   // sub-wave CACHE entries only (0: whole waves)
+    int without_params;  // 1: only for a norm called without gamma and beta
 };
 
 static const TableEntry kTable[] = {
@@ -332,9 +333,10 @@ static lr_plan split_prior(const lr_device_facts* f, int op, int64_t rows, int64
 }
 
 static lr_plan prior_plan(const lr_device_facts* f, int op, int64_t rows, int64_t cols, int policy,
-                          bool aligned, bool allow_split) {
+                          bool aligned, bool allow_split, bool params) {
     auto matches = [&](const TableEntry& e) {
-        return e.op == op && e.policy == policy && e.rows == rows && e.cols == cols && e.aligned == (aligned ? 1 : 0);
+        return e.op == op && e.policy == policy && e.rows == rows && e.cols == cols &&
+               e.aligned == (aligned ? 1 : 0) && (e.without_params == 0 || !params);
     };
     auto from_entry = [&](const TableEntry& e) {
         return make_plan(e.family, e.S, e.Q, e.nch, rows, cols, op, aligned, e.splits, e.lanes);
@@ -433,13 +435,29 @@ extern "C" void lr_device_facts_mi355x(lr_device_facts* out) {
     out->wave_size = 64;
 }
 
+namespace lr {
+
+lr_status plan_for_call(const lr_device_facts* facts, int op, int64_t rows, int64_t cols, int policy,
+                        bool row_aligned, bool allow_split, bool params, lr_plan* out) {
+    lr_status st = check_problem(facts, op, rows, cols, policy);
+    if (st != LR_OK) return st;
+    const bool aligned = row_aligned && cols % kVec == 0;
+    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned, allow_split, params);
+    st = validate_plan(facts, op, rows, cols, policy, aligned, &p);
+    if (st != LR_OK) return st;
+    *out = p;
+    return LR_OK;
+}
+
+}  // namespace lr
+
 extern "C" lr_status lr_plan_for_device(const lr_device_facts* facts, lr_op op, int64_t rows, int64_t cols,
                                         lr_reduction_policy policy, int32_t row_aligned, lr_plan* out) {
     lr_status st = check_problem(facts, op, rows, cols, policy);
     if (st != LR_OK) return st;
     if (out == nullptr) return LR_ERR_NULL_POINTER;
     const bool aligned = row_aligned != 0 && cols % kVec == 0;
-    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned, false);
+    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned, false, true);
     st = validate_plan(facts, op, rows, cols, policy, aligned, &p);
     if (st != LR_OK) return st;
     *out = p;
@@ -452,7 +470,7 @@ extern "C" lr_status lr_plan_for_device_ws(const lr_device_facts* facts, lr_op o
     if (st != LR_OK) return st;
     if (out == nullptr) return LR_ERR_NULL_POINTER;
     const bool aligned = row_aligned != 0 && cols % kVec == 0;
-    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned, true);
+    lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned, true, true);
     st = validate_plan(facts, op, rows, cols, policy, aligned, &p);
     if (st != LR_OK) return st;
     *out = p;

@@ -32,8 +32,9 @@ copy, both ways, under every one-row CACHE plan it compiles: its fastest is
 the floor of a launch of this size.
 
 RMSNorm and LayerNorm, 768 x 6144, with and without their per-column
-parameters (gamma; gamma and beta), each at the plan the library picks and
-at six waves per row, cold (32 rotating buffer sets, as the bench): the
+parameters (gamma; gamma and beta), each at the plan the library picks for
+that call (RMSNorm without gamma has a plan of its own) and at six waves per
+row, cold (32 rotating buffer sets, as the bench): the
 difference is what reading the parameters after the row's reductions costs
 a launch, although they add no HBM traffic (they are L2 hits).
 """
@@ -238,7 +239,15 @@ def main(argv=None):
                 # raw calls on precomputed pointers: the host must outpace the
                 # GPU's 7 us per launch
                 g_, b_ = (gp, bp) if with_p else (None, None)
-                if op == "rmsnorm":
+                if pname == "auto":
+                    # the typed call: a norm without its parameters may take
+                    # a plan of its own
+                    if op == "rmsnorm":
+                        fn = (lambda k, g_=g_: lr.lib.lr_rmsnorm_f32(xp[k], g_, yp[k], rows, cols, 1e-6, 0, sh))
+                    else:
+                        fn = (lambda k, g_=g_, b_=b_: lr.lib.lr_layernorm_f32(
+                            xp[k], g_, b_, yp[k], rows, cols, 1e-5, 0, sh))
+                elif op == "rmsnorm":
                     fn = (lambda k, pp=pp, g_=g_: lr.lib.lr_rmsnorm_f32_with_plan(
                         xp[k], g_, yp[k], rows, cols, 1e-6, 0, pp, sh))
                 else:

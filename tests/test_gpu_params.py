@@ -80,3 +80,33 @@ def test_parameters_off_the_grid(op, rows, cols):
             assert st == lr.LR_OK, (what, lr.lr_status_string(st))
             assert guards_intact(yv, yf), what
             assert_parity(yv.cpu().numpy(), ref, what)
+
+
+def test_rmsnorm_without_gamma_takes_its_own_plan():
+    """RMSNorm 768x6144 called without gamma launches the plan listed for that
+    case (five waves of six chunks per row), not the four waves of six of the
+    call with gamma: its output equals that explicit plan's bit for bit (the
+    unordered tree is fixed by the plan) and the double oracle within the
+    stated bound ("TIRx Metal reduction lowering", section 8, the affine step
+    skipped when no scale is given)"""
+    rows, cols = 768, 6144
+    d = synth.rmsnorm_inputs(rows, cols, seed=21)
+    x = d["x"]
+    ref = oracle.rmsnorm(x, None, EPS["rmsnorm"])
+    facts = lr.lr_device_facts_query()
+    with_gamma = lr.lr_plan_query("rmsnorm", rows, cols, "unordered_tree")
+    own = next(p for p in lr.lr_plan_enumerate(facts, "rmsnorm", rows, cols, "unordered_tree", 1)
+               if p.family == lr.LR_FAMILY_CACHE and p.waves_per_row == 5 and p.chunks_per_lane == 6
+               and p.rows_per_block == 1)
+    assert (with_gamma.waves_per_row, with_gamma.chunks_per_lane) != (5, 6)
+    xv = torch.from_numpy(x).to(DEV)
+    outs = {}
+    for name, plan in (("auto", None), ("own", own), ("with_gamma_plan", with_gamma)):
+        print(f"\n[gpu] rmsnorm {rows}x{cols} without gamma plan={name}", flush=True)
+        y = torch.zeros_like(xv)
+        st = lr.lr_rmsnorm_f32(xv, None, y, rows, cols, EPS["rmsnorm"], plan=plan)
+        torch.cuda.synchronize()
+        assert st == lr.LR_OK, (name, lr.lr_status_string(st))
+        outs[name] = y.cpu().numpy()
+        assert_parity(outs[name], ref, f"rmsnorm without gamma, plan {name}")
+    assert np.array_equal(outs["auto"].view(np.uint32), outs["own"].view(np.uint32))
