@@ -146,7 +146,12 @@ def main(argv=None):
                          "family one of cache, stream, ordered, tree, split; N is the split count of a "
                          "split plan, the lanes per row of a sub-wave cache plan")
     ap.add_argument("--rounds", type=int, default=6)
+    ap.add_argument("--no-params", action="store_true",
+                    help="RMSNorm / LayerNorm called without gamma and beta ('auto' is then the typed call's "
+                         "plan, which may be one listed for that case)")
     args = ap.parse_args(argv)
+    if args.no_params and args.op not in ("rmsnorm", "layernorm", "add_layernorm"):
+        raise SystemExit("--no-params applies to the norms")
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -168,6 +173,8 @@ def main(argv=None):
         ys = [torch.empty_like(x0) for _ in range(sets)]
     g = torch.rand(cols, device=dev, generator=gen) + 0.5
     b = torch.randn(cols, device=dev, generator=gen) * 0.1
+    if args.no_params:
+        g = b = None
     lab = torch.randint(0, cols, (rows,), device=dev, generator=gen)
     rs = [torch.randn(rows, cols, device=dev, generator=gen) for _ in range(sets)] if op == "add_layernorm" else None
     ws = torch.empty(rows * 64 * 8, dtype=torch.uint8, device=dev)  # the largest split: 64 segments
@@ -175,7 +182,9 @@ def main(argv=None):
 
     facts = lr.lr_device_facts_query()
     aligned = 1 if cols % 4 == 0 else 0
-    auto = lr.lr_plan_query(op, rows, cols, args.policy)
+    # without parameters a norm's typed call may take a plan of its own,
+    # which the plan query does not report: time the call itself (plan None)
+    auto = None if args.no_params else lr.lr_plan_query(op, rows, cols, args.policy)
     lr.check(run(0, auto), "automatic plan")
     torch.cuda.synchronize()
     ref = ys[0].double().clone()
@@ -217,9 +226,13 @@ def main(argv=None):
            "ordered_tree": "LR_ORDERED_TREE", "fold_right": "LR_FOLD_RIGHT"}[args.policy]
 
     def table_line(p):
-        tail = f", {p.splits}" if p.family == lr.LR_FAMILY_SPLIT else ""
-        if p.lanes_per_row < 64:
-            tail = f", 0, {p.lanes_per_row}"
+        splits = p.splits if p.family == lr.LR_FAMILY_SPLIT else 0
+        lanes = p.lanes_per_row if p.lanes_per_row < 64 else 0
+        # trailing fields: splits, lanes per row, 1 for a no-parameter entry
+        extra = [splits, lanes] + ([1] if args.no_params else [])
+        while extra and extra[-1] == 0:
+            extra.pop()
+        tail = "".join(f", {v}" for v in extra)
         return (f"{{{opn}, {pol}, {rows}, {cols}, {aligned}, {fam[p.family]}, {p.waves_per_row}, "
                 f"{p.rows_per_block}, {p.chunks_per_lane}{tail}}},")
     # the best plan, and the best that needs no workspace (the typed entry
