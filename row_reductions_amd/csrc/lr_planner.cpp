@@ -441,6 +441,7 @@ lr_status plan_for_call(const lr_device_facts* facts, int op, int64_t rows, int6
                         bool row_aligned, bool allow_split, bool params, lr_plan* out) {
     lr_status st = check_problem(facts, op, rows, cols, policy);
     if (st != LR_OK) return st;
+    if (out == nullptr) return LR_ERR_NULL_POINTER;
     const bool aligned = row_aligned && cols % kVec == 0;
     lr_plan p = prior_plan(facts, op, rows, cols, policy, aligned, allow_split, params);
     st = validate_plan(facts, op, rows, cols, policy, aligned, &p);
